@@ -1,0 +1,140 @@
+/*
+ * santa.h — C ABI of the MI355X (gfx950) SANTA / S²ANTA decode-attention library (libsanta.so).
+ *
+ * One decode step of stochastic sparse attention, as defined in "Stochastic Sparse Attention for
+ * Memory-Bound Inference" (Lee et al., arXiv:2605.01910):
+ *   1. scores s = q K^T / sqrt(dk) over the whole KV cache (Section 2, Eq. 1), exact, or with the
+ *      Bernoulli ternary query of Section 5 (Eq. 5) and Appendix C (Eqs. 8-9);
+ *   2. the softmax over the nk keys and its CDF, built from per-chunk max / sum-exp statistics
+ *      (Section 3.1, split-KV; Appendix O, Algorithms 3-4);
+ *   3. S indices drawn from the post-softmax categorical by inverse CDF: i.i.d. (SANTA, Section 2,
+ *      Eq. 4), stratified or systematic (S²ANTA, Section 2.1), with the half-open convention
+ *      1{F(j-1) <= t < F(j)} of Appendix A.4;
+ *   4. a gather-and-add of the sampled V rows, each row read once per GQA group and weighted by its
+ *      sample count (Appendix O, Algorithm 5), scaled by 1/S (Section 2, Eq. 4).
+ *
+ * Conventions shared by every entry point:
+ *   - Device pointers are caller-owned; the library never frees or retains them past the call.
+ *   - Layouts are row-major: q and out are [batch, heads, d]; K and V are sequence-major caches
+ *     [batch, nk, kv_heads, d] (Appendix Q), element (b, n, k, i) at
+ *     b*kv_batch_stride + n*kv_seq_stride + k*d + i. Query head h reads KV head h / (heads/kv_heads)
+ *     (Appendix O, Algorithm 2).
+ *   - K and V rows and q must be 16-byte aligned (base pointers and strides).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default stream). Results are valid
+ *     after the stream is synchronised. Debug outputs that live on the host (stats, stage times) make
+ *     the call synchronise the stream before it returns.
+ *   - Every call validates its arguments on the host before it makes any HIP call, and returns a
+ *     status code (SANTA_OK or a SANTA_ERR_*); nothing is thrown across the ABI. A description of the
+ *     last failure on the calling thread is available from santa_last_error().
+ *   - The result is a pure function of (inputs, S, mode, seed): the random numbers are Philox4x32-10
+ *     (Salmon et al., SC'11) keyed by (seed mod 2^32, seed >> 32) with counter (m, h, b, tag): tag 0 for
+ *     the m-th i.i.d./stratified point of query head h in batch b, tag 1 for the systematic offset, tag
+ *     2 + 256n for the Bernoulli decision of query element m in Bernoulli sample n. A uniform is
+ *     ((x0 << 32 | x1) >> 11) * 2^-53.
+ *   - Inputs must be finite; NaN and Inf are not checked and propagate.
+ */
+#ifndef SANTA_H_
+#define SANTA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define SANTA_OK 0
+#define SANTA_ERR_INVALID_ARG 1     /* null pointer, heads % kv_heads != 0, S < 1, nk < 1, bad mode bits ... */
+#define SANTA_ERR_UNSUPPORTED 2     /* d not in {64, 128}, dtype, sizes beyond the kernels' limits */
+#define SANTA_ERR_WORKSPACE 3       /* workspace_bytes smaller than santa_workspace_bytes() */
+#define SANTA_ERR_HIP 4             /* a HIP runtime call or launch failed (see santa_last_error) */
+
+/* sampling modes (low byte) and flags */
+#define SANTA_IID 0                 /* SANTA: T_m ~ U[0,1) i.i.d. (Section 2, Eq. 4) */
+#define SANTA_STRAT 1               /* S²ANTA-strat: T_m ~ U[m/S, (m+1)/S) independently (Section 2.1) */
+#define SANTA_SYS 2                 /* S²ANTA-sys: one U ~ U[0, 1/S), T_m = U + m/S (Section 2.1) */
+#define SANTA_TERNARY_Q 0x100       /* Bernoulli ternary query for the score stage (Section 5, Eq. 5; B = 1,
+                                       norm = max_i |q_i| per (batch, head)) */
+
+/* element types of q, K, V and out */
+#define SANTA_BF16 0
+#define SANTA_F32 1
+
+typedef struct santa_stats {
+  int32_t launches;      /* kernels launched by the call */
+  int64_t bytes_k;       /* K bytes streamed: batch * nk * kv_heads * d * elt */
+  int64_t bytes_v;       /* V bytes gathered: (sum over (b, kv) of distinct sampled rows) * d * elt */
+  int64_t bytes_qo;      /* q read + out written: 2 * batch * heads * d * elt */
+  int64_t unique_rows;   /* sum over (b, kv) of the distinct sampled rows */
+} santa_stats;
+
+typedef struct santa_args {
+  const void* q;             /* [batch, heads, d] device */
+  const void* K;             /* [batch, nk, kv_heads, d] device (strided, see above) */
+  const void* V;             /* same layout as K */
+  void* out;                 /* [batch, heads, d] device, same dtype as the inputs */
+  int32_t batch;
+  int32_t heads;
+  int32_t kv_heads;
+  int32_t d;                 /* head dimension: 64 or 128 */
+  int64_t nk;                /* keys attended per sequence (the current token included) */
+  int64_t kv_seq_stride;     /* elements between consecutive positions; 0 means kv_heads * d */
+  int64_t kv_batch_stride;   /* elements between sequences; 0 means nk * kv_seq_stride */
+  int32_t S;                 /* samples per query head, >= 1 */
+  int32_t mode;              /* SANTA_IID | SANTA_STRAT | SANTA_SYS, optionally | SANTA_TERNARY_Q */
+  int32_t dtype;             /* SANTA_BF16 or SANTA_F32 */
+  int32_t reserved0;
+  uint64_t seed;
+  void* stream;              /* hipStream_t, NULL = default stream */
+  void* workspace;           /* device scratch of at least santa_workspace_bytes() bytes */
+  size_t workspace_bytes;
+  /* optional debug outputs; NULL to skip */
+  int32_t* idx_out;          /* device [batch, heads, S]: sampled key index of each point, in point order */
+  double* prob_out;          /* device [batch, heads, nk]: softmax probabilities */
+  santa_stats* stats_out;    /* host; the call synchronises the stream to fill it */
+  float* stage_ms;           /* host float[4]: per-kernel GPU time (events); synchronises the stream */
+} santa_args;
+
+/*
+ * santa_decode — one SANTA / S²ANTA decode step in its simplest form: batch 1, bf16 q/K/V/out,
+ * contiguous [nk, kv_heads, d] caches, the default stream, and a workspace the library allocates on
+ * first use and keeps (grow-only) until santa_release(). Returns a status code.
+ */
+int santa_decode(const void* q, const void* K, const void* V, int64_t nk, int heads, int kv_heads, int d, int S,
+                 int mode, uint64_t seed, void* out);
+
+/*
+ * santa_decode_ex — the full form. Caller-owned workspace (`workspace`, `workspace_bytes`); never
+ * allocates device memory. Launches the score, sampling and gather kernels on `stream`.
+ */
+int santa_decode_ex(const santa_args* a);
+
+/* Workspace bytes santa_decode_ex needs for these sizes (0 if the sizes are invalid). */
+size_t santa_workspace_bytes(int batch, int64_t nk, int heads, int kv_heads, int d, int S, int mode);
+
+/*
+ * santa_dense_decode — dense decode attention softmax(q K^T / sqrt(dk)) V (Section 2, Eq. 1) over the
+ * same layouts, fp32 accumulation, output in the input dtype. A measurement baseline that reads all of
+ * K and V (split-KV partials and a merge, as in FlashDecoding-style decoding). S, mode, seed and the
+ * debug outputs of `a` are ignored; the workspace must hold santa_dense_workspace_bytes() bytes.
+ */
+int santa_dense_decode(const santa_args* a);
+size_t santa_dense_workspace_bytes(int batch, int64_t nk, int heads, int kv_heads, int d);
+
+/*
+ * santa_philox4x32_10 — host-side evaluation of the library's own Philox4x32-10 (the same inline code
+ * the kernels run), for known-answer tests: out = Philox(ctr, key).
+ */
+void santa_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+
+const char* santa_status_string(int status);
+const char* santa_last_error(void);   /* thread-local description of the last failure, "" if none */
+const char* santa_version(void);
+void santa_release(void);            /* frees the workspace santa_decode allocated, on every device */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SANTA_H_ */

@@ -1,0 +1,253 @@
+"""Python binding of libsanta.so, the MI355X (gfx950) SANTA / S²ANTA decode-attention library.
+
+Argument marshalling only: every step of the decode runs in the library's HIP kernels. PyTorch provides
+device memory and the current stream. The entry points mirror include/santa.h:
+
+    decode(q, K, V, S, mode, seed, ...)      -> santa_decode_ex
+    decode_simple(q, K, V, S, mode, seed)    -> santa_decode (library-owned workspace, batch 1, bf16)
+    dense_decode(q, K, V, ...)               -> santa_dense_decode (dense baseline)
+    workspace_bytes(...), dense_workspace_bytes(...), philox4x32_10(ctr, key), version(), last_error()
+
+Shapes: q [B, H, d]; K, V [B, nk, Hkv, d] (the sequence dimension may be strided, e.g. a preallocated
+cache with room for more positions); out [B, H, d]. dtype bf16 or fp32.
+
+The library is built in-tree (``python -m stochastic_sparse_attention_split_amd._build`` or
+``__graft_entry__.build()``); importing works without it, but every call raises if it is missing.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsanta.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+IID, STRAT, SYS = 0, 1, 2
+TERNARY_Q = 0x100
+BF16, F32 = 0, 1
+MODES = {"iid": IID, "strat": STRAT, "sys": SYS}
+
+EXPORTED = [
+    "santa_decode", "santa_decode_ex", "santa_workspace_bytes", "santa_dense_decode",
+    "santa_dense_workspace_bytes", "santa_philox4x32_10", "santa_status_string", "santa_last_error",
+    "santa_version", "santa_release",
+]
+
+
+class SantaStats(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int32), ("bytes_k", ctypes.c_int64), ("bytes_v", ctypes.c_int64),
+                ("bytes_qo", ctypes.c_int64), ("unique_rows", ctypes.c_int64)]
+
+
+class SantaArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("K", ctypes.c_void_p), ("V", ctypes.c_void_p), ("out", ctypes.c_void_p),
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("nk", ctypes.c_int64), ("kv_seq_stride", ctypes.c_int64), ("kv_batch_stride", ctypes.c_int64),
+        ("S", ctypes.c_int32), ("mode", ctypes.c_int32), ("dtype", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("seed", ctypes.c_uint64), ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t), ("idx_out", ctypes.c_void_p), ("prob_out", ctypes.c_void_p),
+        ("stats_out", ctypes.POINTER(SantaStats)), ("stage_ms", ctypes.POINTER(ctypes.c_float)),
+    ]
+
+
+class SantaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"santa status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libsanta.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first (stochastic_sparse_attention_split_amd._build)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.santa_decode.restype = ctypes.c_int
+        L.santa_decode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                   ctypes.c_void_p]
+        L.santa_decode_ex.restype = ctypes.c_int
+        L.santa_decode_ex.argtypes = [ctypes.POINTER(SantaArgs)]
+        L.santa_dense_decode.restype = ctypes.c_int
+        L.santa_dense_decode.argtypes = [ctypes.POINTER(SantaArgs)]
+        L.santa_workspace_bytes.restype = ctypes.c_size_t
+        L.santa_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int]
+        L.santa_dense_workspace_bytes.restype = ctypes.c_size_t
+        L.santa_dense_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.c_int]
+        L.santa_philox4x32_10.restype = None
+        L.santa_philox4x32_10.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32),
+                                          ctypes.POINTER(ctypes.c_uint32)]
+        L.santa_status_string.restype = ctypes.c_char_p
+        L.santa_status_string.argtypes = [ctypes.c_int]
+        L.santa_last_error.restype = ctypes.c_char_p
+        L.santa_last_error.argtypes = []
+        L.santa_version.restype = ctypes.c_char_p
+        L.santa_version.argtypes = []
+        L.santa_release.restype = None
+        L.santa_release.argtypes = []
+        _lib = L
+    return _lib
+
+
+def version() -> str:
+    return lib().santa_version().decode()
+
+
+def last_error() -> str:
+    return lib().santa_last_error().decode()
+
+
+def _check(status: int):
+    if status != OK:
+        raise SantaError(status, last_error() or lib().santa_status_string(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}: bf16 or fp32 expected")
+
+
+def _mode_code(mode, ternary: bool) -> int:
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    return m | (TERNARY_Q if ternary else 0)
+
+
+def workspace_bytes(B: int, nk: int, H: int, Hkv: int, d: int, S: int, mode=STRAT) -> int:
+    return int(lib().santa_workspace_bytes(B, nk, H, Hkv, d, S, _mode_code(mode, False)))
+
+
+def dense_workspace_bytes(B: int, nk: int, H: int, Hkv: int, d: int) -> int:
+    return int(lib().santa_dense_workspace_bytes(B, nk, H, Hkv, d))
+
+
+def _fill_common(a: SantaArgs, q, K, V, out, nk, stream):
+    if q.dim() != 3 or K.dim() != 4 or V.dim() != 4:
+        raise ValueError("q must be [B, H, d]; K and V [B, nk, Hkv, d]")
+    if K.shape != V.shape or K.stride() != V.stride():
+        raise ValueError("K and V must have the same shape and strides")
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous")
+    if K.stride(3) != 1 or K.stride(2) != K.shape[3]:
+        raise ValueError("K/V rows must be contiguous [Hkv, d] per position")
+    if not (q.dtype == K.dtype == V.dtype == out.dtype):
+        raise TypeError("q, K, V and out must share one dtype")
+    B, H, d = q.shape
+    a.q, a.K, a.V, a.out = q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr()
+    a.batch, a.heads, a.kv_heads, a.d = B, H, K.shape[2], d
+    a.nk = K.shape[1] if nk is None else int(nk)
+    a.kv_seq_stride = K.stride(1)
+    a.kv_batch_stride = K.stride(0)
+    a.dtype = _dtype_code(q)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    a.stream = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="strat", seed: int = 0, *,
+           ternary: bool = False, nk: int | None = None, out: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None, idx_out: torch.Tensor | None = None,
+           prob_out: torch.Tensor | None = None, stats: bool = False, stage_ms: bool = False, stream=None):
+    """One SANTA / S²ANTA decode step through santa_decode_ex.
+
+    Returns out, or (out, info) when stats or stage_ms is requested (info holds the stats fields and the
+    per-kernel milliseconds [score, sample, gather, total]).
+    """
+    if out is None:
+        out = torch.empty_like(q)
+    a = SantaArgs()
+    _fill_common(a, q, K, V, out, nk, stream)
+    a.S = int(S)
+    a.mode = _mode_code(mode, ternary)
+    a.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    need = int(lib().santa_workspace_bytes(a.batch, a.nk, a.heads, a.kv_heads, a.d, a.S, a.mode))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    if idx_out is not None:
+        if idx_out.dtype != torch.int32 or idx_out.numel() < a.batch * a.heads * a.S:
+            raise ValueError("idx_out must be int32 with batch*heads*S elements")
+        a.idx_out = idx_out.data_ptr()
+    if prob_out is not None:
+        if prob_out.dtype != torch.float64 or prob_out.numel() < a.batch * a.heads * a.nk:
+            raise ValueError("prob_out must be float64 with batch*heads*nk elements")
+        a.prob_out = prob_out.data_ptr()
+    st = SantaStats()
+    ms = (ctypes.c_float * 4)()
+    if stats:
+        a.stats_out = ctypes.pointer(st)
+    if stage_ms:
+        a.stage_ms = ms
+    _check(lib().santa_decode_ex(ctypes.byref(a)))
+    if stats or stage_ms:
+        info = {}
+        if stats:
+            info.update({f: getattr(st, f) for f, _ in SantaStats._fields_})
+        if stage_ms:
+            info["stage_ms"] = list(ms)
+        return out, info
+    return out
+
+
+def decode_simple(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="strat", seed: int = 0, *,
+                  ternary: bool = False, out: torch.Tensor | None = None):
+    """santa_decode: batch 1, bf16, contiguous caches, default stream, library-owned workspace."""
+    if out is None:
+        out = torch.empty_like(q)
+    if q.dim() == 3:
+        if q.shape[0] != 1:
+            raise ValueError("santa_decode takes batch 1")
+        q1, K1, V1 = q[0], K[0], V[0]
+    else:
+        q1, K1, V1 = q, K, V
+    for t in (q1, K1, V1, out):
+        if not t.is_contiguous():
+            raise ValueError("santa_decode needs contiguous tensors")
+    nk, Hkv, d = K1.shape
+    H = q1.shape[0]
+    _check(lib().santa_decode(q1.data_ptr(), K1.data_ptr(), V1.data_ptr(), nk, H, Hkv, d, int(S),
+                              _mode_code(mode, ternary), int(seed) & 0xFFFFFFFFFFFFFFFF, out.data_ptr()))
+    return out
+
+
+def dense_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, *, nk: int | None = None,
+                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """Dense decode attention baseline through santa_dense_decode."""
+    if out is None:
+        out = torch.empty_like(q)
+    a = SantaArgs()
+    _fill_common(a, q, K, V, out, nk, stream)
+    need = int(lib().santa_dense_workspace_bytes(a.batch, a.nk, a.heads, a.kv_heads, a.d))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().santa_dense_decode(ctypes.byref(a)))
+    return out
+
+
+def philox4x32_10(ctr, key):
+    """The library's own host-side Philox4x32-10 (the kernels' code path) -> 4 uint32 words."""
+    c = (ctypes.c_uint32 * 4)(*[int(x) & 0xFFFFFFFF for x in ctr])
+    k = (ctypes.c_uint32 * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+    o = (ctypes.c_uint32 * 4)()
+    lib().santa_philox4x32_10(c, k, o)
+    return tuple(int(x) for x in o)
+
+
+def release():
+    lib().santa_release()

@@ -1,0 +1,347 @@
+// C ABI of libsanta.so: argument validation (before any HIP call), workspace layout, and the launch
+// sequence score -> sample -> gather on the caller's stream. See include/santa.h for the contract.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/santa.h"
+#include "common.h"
+#include "launch.h"
+
+using namespace santa;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SANTA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+constexpr size_t LDS_LIMIT = 160 * 1024 - 1024;  // dynamic LDS left beside the kernels' static LDS
+
+struct Layout {
+  size_t stash, cmax, csum, idx, unique, total;
+};
+
+Layout layout(int64_t B, int64_t nk, int64_t H, int64_t Hkv, int64_t S) {
+  const int64_t T = (nk + CHUNK - 1) / CHUNK;
+  Layout L;
+  size_t off = 0;
+  L.stash = off;
+  off = align_up(off + (size_t)(B * H * nk) * sizeof(double));
+  L.cmax = off;
+  off = align_up(off + (size_t)(B * H * T) * sizeof(double));
+  L.csum = off;
+  off = align_up(off + (size_t)(B * H * T) * sizeof(double));
+  L.idx = off;
+  off = align_up(off + (size_t)(B * H * S) * sizeof(int32_t));
+  L.unique = off;
+  off = align_up(off + (size_t)(B * Hkv) * sizeof(int32_t));
+  L.total = off;
+  return L;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// shape checks shared by the sampled and the dense entry points
+int validate_common(const santa_args* a, int64_t* seq, int64_t* bstride) {
+  if (!a) return fail(SANTA_ERR_INVALID_ARG, "args is NULL");
+  if (!a->q || !a->K || !a->V || !a->out) return fail(SANTA_ERR_INVALID_ARG, "q, K, V and out must be non-NULL");
+  if (a->batch < 1 || a->heads < 1 || a->kv_heads < 1 || a->nk < 1)
+    return fail(SANTA_ERR_INVALID_ARG, "batch, heads, kv_heads and nk must be >= 1");
+  if (a->heads % a->kv_heads) return fail(SANTA_ERR_INVALID_ARG, "heads (%d) must be a multiple of kv_heads (%d)",
+                                           a->heads, a->kv_heads);
+  if (a->dtype != SANTA_BF16 && a->dtype != SANTA_F32)
+    return fail(SANTA_ERR_UNSUPPORTED, "dtype %d is not SANTA_BF16 or SANTA_F32", a->dtype);
+  if (a->d != 64 && a->d != 128) return fail(SANTA_ERR_UNSUPPORTED, "head dimension %d is not 64 or 128", a->d);
+  if (a->heads / a->kv_heads > MAX_GROUP)
+    return fail(SANTA_ERR_UNSUPPORTED, "GQA group %d exceeds %d heads per KV head", a->heads / a->kv_heads, MAX_GROUP);
+  if (a->nk > (int64_t)MAX_CHUNKS * CHUNK)
+    return fail(SANTA_ERR_UNSUPPORTED, "nk %lld exceeds %d", (long long)a->nk, MAX_CHUNKS * CHUNK);
+  const int64_t row = (int64_t)a->kv_heads * a->d;
+  const int64_t s = a->kv_seq_stride ? a->kv_seq_stride : row;
+  if (s < row) return fail(SANTA_ERR_INVALID_ARG, "kv_seq_stride %lld < kv_heads*d", (long long)s);
+  const int64_t bs = a->kv_batch_stride ? a->kv_batch_stride : s * a->nk;
+  if (a->batch > 1 && bs < s * a->nk)
+    return fail(SANTA_ERR_INVALID_ARG, "kv_batch_stride %lld < nk*kv_seq_stride", (long long)bs);
+  const int64_t esz = a->dtype == SANTA_BF16 ? 2 : 4;
+  if ((s * esz) % 16 || (bs * esz) % 16 || !aligned16(a->q) || !aligned16(a->K) || !aligned16(a->V))
+    return fail(SANTA_ERR_INVALID_ARG, "q, K, V and the K/V strides must be 16-byte aligned");
+  *seq = s;
+  *bstride = bs;
+  return SANTA_OK;
+}
+
+int validate_sampled(const santa_args* a, int64_t* seq, int64_t* bstride) {
+  int st = validate_common(a, seq, bstride);
+  if (st) return st;
+  if (a->S < 1) return fail(SANTA_ERR_INVALID_ARG, "S must be >= 1 (got %d)", a->S);
+  const int base = a->mode & 0xFF, flags = a->mode & ~0xFF;
+  if (base > SANTA_SYS || base < 0 || (flags & ~SANTA_TERNARY_Q))
+    return fail(SANTA_ERR_INVALID_ARG, "mode 0x%x has unknown bits", (unsigned)a->mode);
+  if (a->S > 65535) return fail(SANTA_ERR_UNSUPPORTED, "S %d exceeds 65535", a->S);
+  const int G = a->heads / a->kv_heads;
+  if (gather_lds_bytes(G, a->S) > LDS_LIMIT)
+    return fail(SANTA_ERR_UNSUPPORTED, "G*S = %d samples per KV group exceed the gather kernel's LDS table", G * a->S);
+  return SANTA_OK;
+}
+
+struct Events {
+  hipEvent_t e[4] = {nullptr, nullptr, nullptr, nullptr};
+  bool on = false;
+  ~Events() {
+    for (auto& x : e)
+      if (x) (void)hipEventDestroy(x);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+size_t santa_workspace_bytes(int batch, int64_t nk, int heads, int kv_heads, int d, int S, int mode) {
+  (void)d;
+  (void)mode;
+  if (batch < 1 || nk < 1 || heads < 1 || kv_heads < 1 || S < 1 || heads % kv_heads) return 0;
+  return layout(batch, nk, heads, kv_heads, S).total;
+}
+
+int santa_decode_ex(const santa_args* a) {
+  g_err.clear();
+  int64_t seq = 0, bstride = 0;
+  int st = validate_sampled(a, &seq, &bstride);
+  if (st) return st;
+  const Layout L = layout(a->batch, a->nk, a->heads, a->kv_heads, a->S);
+  if (!a->workspace || a->workspace_bytes < L.total)
+    return fail(SANTA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", a->workspace_bytes,
+                L.total);
+
+  char* ws = (char*)a->workspace;
+  Problem p;
+  p.q = a->q;
+  p.K = a->K;
+  p.V = a->V;
+  p.out = a->out;
+  p.B = a->batch;
+  p.H = a->heads;
+  p.Hkv = a->kv_heads;
+  p.G = a->heads / a->kv_heads;
+  p.d = a->d;
+  p.nk = a->nk;
+  p.seq_stride = seq;
+  p.batch_stride = bstride;
+  p.S = a->S;
+  p.mode = a->mode & 0xFF;
+  p.ternary = (a->mode & SANTA_TERNARY_Q) != 0;
+  p.bf16 = a->dtype == SANTA_BF16;
+  p.seed = a->seed;
+  p.scale = 1.0 / std::sqrt((double)a->d);
+  p.T = (int)((a->nk + CHUNK - 1) / CHUNK);
+  p.stash = (double*)(ws + L.stash);
+  p.cmax = (double*)(ws + L.cmax);
+  p.csum = (double*)(ws + L.csum);
+  p.idx = a->idx_out ? a->idx_out : (int32_t*)(ws + L.idx);
+  p.unique = (int32_t*)(ws + L.unique);
+  p.prob = a->prob_out;
+
+  hipStream_t stream = (hipStream_t)a->stream;
+  Events ev;
+  if (a->stage_ms) {
+    ev.on = true;
+    for (auto& x : ev.e) {
+      hipError_t e = hipEventCreate(&x);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
+  }
+  hipError_t e;
+  if (ev.on && (e = hipEventRecord(ev.e[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  (void)hipGetLastError();  // start from a clean error state
+  if ((e = launch_score(p, stream)) != hipSuccess) return hip_fail(e, "score kernel launch");
+  if (ev.on && (e = hipEventRecord(ev.e[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if ((e = launch_sample(p, stream)) != hipSuccess) return hip_fail(e, "sample kernel launch");
+  if (ev.on && (e = hipEventRecord(ev.e[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if ((e = launch_gather(p, stream)) != hipSuccess) return hip_fail(e, "gather kernel launch");
+  if (ev.on && (e = hipEventRecord(ev.e[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+
+  if (a->stats_out) {
+    std::vector<int32_t> u((size_t)a->batch * a->kv_heads);
+    if ((e = hipMemcpyAsync(u.data(), p.unique, u.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream)) !=
+        hipSuccess)
+      return hip_fail(e, "hipMemcpyAsync(unique)");
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    int64_t U = 0;
+    for (int32_t x : u) U += x;
+    const int64_t esz = p.bf16 ? 2 : 4;
+    santa_stats* s = a->stats_out;
+    s->launches = 3;
+    s->bytes_k = (int64_t)a->batch * a->nk * a->kv_heads * a->d * esz;
+    s->bytes_v = U * a->d * esz;
+    s->bytes_qo = 2 * (int64_t)a->batch * a->heads * a->d * esz;
+    s->unique_rows = U;
+  }
+  if (ev.on) {
+    if ((e = hipEventSynchronize(ev.e[3])) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    for (int i = 0; i < 3; ++i) {
+      float ms = 0.f;
+      if ((e = hipEventElapsedTime(&ms, ev.e[i], ev.e[i + 1])) != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+      a->stage_ms[i] = ms;
+    }
+    float ms = 0.f;
+    if ((e = hipEventElapsedTime(&ms, ev.e[0], ev.e[3])) != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    a->stage_ms[3] = ms;
+  }
+  return SANTA_OK;
+}
+
+// ---- library-owned workspace for the simple entry point
+
+namespace {
+std::mutex g_ws_mu;
+struct DevWs {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::vector<DevWs> g_ws;
+}  // namespace
+
+int santa_decode(const void* q, const void* K, const void* V, int64_t nk, int heads, int kv_heads, int d, int S,
+                 int mode, uint64_t seed, void* out) {
+  g_err.clear();
+  santa_args a;
+  std::memset(&a, 0, sizeof a);
+  a.q = q;
+  a.K = K;
+  a.V = V;
+  a.out = out;
+  a.batch = 1;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.d = d;
+  a.nk = nk;
+  a.S = S;
+  a.mode = mode;
+  a.dtype = SANTA_BF16;
+  a.seed = seed;
+  int64_t seq, bs;
+  int st = validate_sampled(&a, &seq, &bs);
+  if (st) return st;
+  const size_t need = layout(1, nk, heads, kv_heads, S).total;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+  DevWs& w = g_ws[dev];
+  if (w.bytes < need) {
+    if (w.ptr) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    if ((e = hipMalloc(&w.ptr, need)) != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
+    w.bytes = need;
+  }
+  a.workspace = w.ptr;
+  a.workspace_bytes = w.bytes;
+  return santa_decode_ex(&a);
+}
+
+void santa_release(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) cur = -1;
+  for (size_t dev = 0; dev < g_ws.size(); ++dev) {
+    if (!g_ws[dev].ptr) continue;
+    if (hipSetDevice((int)dev) == hipSuccess) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(g_ws[dev].ptr);
+    }
+    g_ws[dev] = DevWs{};
+  }
+  if (cur >= 0) (void)hipSetDevice(cur);
+}
+
+// ---- dense baseline
+
+size_t santa_dense_workspace_bytes(int batch, int64_t nk, int heads, int kv_heads, int d) {
+  if (batch < 1 || nk < 1 || heads < 1 || kv_heads < 1 || heads % kv_heads || (d != 64 && d != 128)) return 0;
+  const int64_t Td = (nk + DENSE_CHUNK - 1) / DENSE_CHUNK;
+  return align_up((size_t)(batch * (int64_t)heads * Td * (d + 2)) * sizeof(float));
+}
+
+int santa_dense_decode(const santa_args* a) {
+  g_err.clear();
+  int64_t seq = 0, bs = 0;
+  int st = validate_common(a, &seq, &bs);
+  if (st) return st;
+  const size_t need = santa_dense_workspace_bytes(a->batch, a->nk, a->heads, a->kv_heads, a->d);
+  if (!a->workspace || a->workspace_bytes < need)
+    return fail(SANTA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", a->workspace_bytes, need);
+  DenseProblem p;
+  p.q = a->q;
+  p.K = a->K;
+  p.V = a->V;
+  p.out = a->out;
+  p.B = a->batch;
+  p.H = a->heads;
+  p.Hkv = a->kv_heads;
+  p.G = a->heads / a->kv_heads;
+  p.d = a->d;
+  p.nk = a->nk;
+  p.seq_stride = seq;
+  p.batch_stride = bs;
+  p.bf16 = a->dtype == SANTA_BF16;
+  p.scale = (float)(1.0 / std::sqrt((double)a->d));
+  p.Td = (int)((a->nk + DENSE_CHUNK - 1) / DENSE_CHUNK);
+  p.part = (float*)a->workspace;
+  (void)hipGetLastError();
+  const hipError_t e = launch_dense(p, (hipStream_t)a->stream);
+  if (e != hipSuccess) return hip_fail(e, "dense kernel launch");
+  return SANTA_OK;
+}
+
+// ---- diagnostics
+
+void santa_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  const Philox4 r = philox4x32_10(ctr[0], ctr[1], ctr[2], ctr[3], key[0], key[1]);
+  out[0] = r.x0;
+  out[1] = r.x1;
+  out[2] = r.x2;
+  out[3] = r.x3;
+}
+
+const char* santa_status_string(int status) {
+  switch (status) {
+    case SANTA_OK: return "ok";
+    case SANTA_ERR_INVALID_ARG: return "invalid argument";
+    case SANTA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SANTA_ERR_WORKSPACE: return "workspace too small";
+    case SANTA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* santa_last_error(void) { return g_err.c_str(); }
+
+const char* santa_version(void) { return "santa-mi355x 0.1.0 (gfx950)"; }
+
+}  // extern "C"

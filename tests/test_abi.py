@@ -1,0 +1,130 @@
+"""The C ABI without a GPU: symbols, constants, argument validation (which runs before any HIP call),
+workspace sizing, and the library's own host-side Philox against the oracle's."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import stochastic_sparse_attention_split_amd as santa
+from oracle import philox
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "santa.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(santa.LIB_PATH):
+        from stochastic_sparse_attention_split_amd import _build
+        _build.build()
+    return santa.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(santa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_functions()
+    assert set(names) == set(santa.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define\s+(SANTA_[A-Z0-9_]+)\s+(0x[0-9a-fA-F]+|\d+)", text))
+    val = {k: int(v, 0) for k, v in defs.items()}
+    assert val["SANTA_IID"] == santa.IID and val["SANTA_STRAT"] == santa.STRAT and val["SANTA_SYS"] == santa.SYS
+    assert val["SANTA_TERNARY_Q"] == santa.TERNARY_Q
+    assert val["SANTA_BF16"] == santa.BF16 and val["SANTA_F32"] == santa.F32
+    assert val["SANTA_OK"] == santa.OK and val["SANTA_ERR_HIP"] == santa.ERR_HIP
+
+
+def _args(**kw):
+    a = santa.SantaArgs()
+    base = dict(q=0x1000, K=0x2000, V=0x3000, out=0x4000, batch=1, heads=8, kv_heads=2, d=128, nk=1000, S=16,
+                mode=santa.STRAT, dtype=santa.BF16, seed=1, workspace=0x5000, workspace_bytes=1 << 40)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), santa.ERR_INVALID_ARG),
+    (dict(out=0), santa.ERR_INVALID_ARG),
+    (dict(heads=6, kv_heads=4), santa.ERR_INVALID_ARG),
+    (dict(S=0), santa.ERR_INVALID_ARG),
+    (dict(nk=0), santa.ERR_INVALID_ARG),
+    (dict(batch=0), santa.ERR_INVALID_ARG),
+    (dict(mode=3), santa.ERR_INVALID_ARG),
+    (dict(mode=0x200), santa.ERR_INVALID_ARG),
+    (dict(d=96), santa.ERR_UNSUPPORTED),
+    (dict(dtype=7), santa.ERR_UNSUPPORTED),
+    (dict(heads=32, kv_heads=2), santa.ERR_UNSUPPORTED),
+    (dict(nk=(1 << 20) + 1), santa.ERR_UNSUPPORTED),
+    (dict(S=70000), santa.ERR_UNSUPPORTED),
+    (dict(heads=16, kv_heads=2, S=4096), santa.ERR_UNSUPPORTED),
+    (dict(kv_seq_stride=100), santa.ERR_INVALID_ARG),
+    (dict(kv_seq_stride=257), santa.ERR_INVALID_ARG),
+    (dict(K=0x2008), santa.ERR_INVALID_ARG),
+    (dict(batch=2, kv_batch_stride=256 * 999), santa.ERR_INVALID_ARG),
+    (dict(workspace_bytes=100), santa.ERR_WORKSPACE),
+    (dict(workspace=0), santa.ERR_WORKSPACE),
+])
+def test_validation_rejects_before_any_hip_call(L, kw, code):
+    a = _args(**kw)
+    assert L.santa_decode_ex(ctypes.byref(a)) == code
+    assert santa.last_error() != ""
+
+
+def test_null_args_and_dense_validation(L):
+    assert L.santa_decode_ex(None) == santa.ERR_INVALID_ARG
+    assert L.santa_dense_decode(None) == santa.ERR_INVALID_ARG
+    a = _args(d=80)
+    assert L.santa_dense_decode(ctypes.byref(a)) == santa.ERR_UNSUPPORTED
+    a = _args(workspace_bytes=4)
+    assert L.santa_dense_decode(ctypes.byref(a)) == santa.ERR_WORKSPACE
+    # the simple entry point validates before it allocates
+    assert L.santa_decode(None, None, None, 100, 8, 2, 128, 16, 1, 0, None) == santa.ERR_INVALID_ARG
+    assert L.santa_decode(1, 1, 1, 100, 8, 2, 100, 16, 1, 0, 1) == santa.ERR_UNSUPPORTED
+
+
+def test_workspace_bytes(L):
+    B, nk, H, Hkv, S = 2, 1000, 8, 2, 16
+    T = (nk + 255) // 256
+    n = santa.workspace_bytes(B, nk, H, Hkv, 128, S)
+    assert n >= B * H * nk * 8 + 2 * B * H * T * 8 + B * H * S * 4 + B * Hkv * 4
+    assert n % 256 == 0
+    assert santa.workspace_bytes(1, 0, 8, 2, 128, S) == 0
+    assert santa.workspace_bytes(1, 10, 6, 4, 128, S) == 0
+    assert santa.dense_workspace_bytes(1, 1024, 8, 2, 128) >= 8 * 2 * 130 * 4
+    assert santa.dense_workspace_bytes(1, 1024, 8, 2, 96) == 0
+
+
+def test_library_philox_matches_oracle(L):
+    rng = np.random.default_rng(1)
+    for _ in range(300):
+        c = [int(x) for x in rng.integers(0, 2**32, 4)]
+        k = [int(x) for x in rng.integers(0, 2**32, 2)]
+        want = tuple(int(x) for x in philox.philox4x32_10(*c, *k))
+        assert santa.philox4x32_10(c, k) == want
+
+
+def test_status_strings_and_version(L):
+    assert santa.version().startswith("santa-mi355x")
+    for s in range(5):
+        assert L.santa_status_string(s)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(santa, "_lib", None)
+    monkeypatch.setattr(santa, "LIB_PATH", "/nonexistent/libsanta.so")
+    with pytest.raises(RuntimeError):
+        santa.lib()

@@ -1,0 +1,216 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded inputs.
+
+Every case prints its label before it touches the GPU. Sizes span several 256-key chunks and ragged
+tails; the full-size workloads are the ones the benchmark times.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import stochastic_sparse_attention_split_amd as santa
+import workloads
+from tests.parity import compare, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    santa.lib()  # raises if the library was not built
+    yield
+
+
+SMALL = [
+    # B, H, Hkv, d, nk, dtype, mode, S, ternary, spikes
+    (1, 1, 1, 64, 1024, "f32", "iid", 16, False, 0),
+    (1, 1, 1, 64, 1024, "f32", "strat", 16, False, 0),
+    (1, 1, 1, 64, 1024, "f32", "sys", 16, False, 0),
+    (1, 4, 1, 128, 1, "bf16", "strat", 16, False, 0),
+    (1, 4, 1, 128, 2, "bf16", "iid", 5, False, 0),
+    (1, 4, 1, 128, 3, "bf16", "sys", 3, False, 0),
+    (1, 4, 1, 128, 8, "bf16", "strat", 4, False, 0),
+    (1, 4, 1, 128, 255, "bf16", "strat", 16, False, 2),
+    (1, 4, 1, 128, 256, "bf16", "sys", 16, False, 2),
+    (1, 4, 1, 128, 257, "bf16", "iid", 16, False, 2),
+    (2, 8, 2, 128, 1000, "bf16", "strat", 100, False, 4),
+    (1, 8, 8, 128, 4097, "bf16", "sys", 64, False, 3),
+    (2, 8, 4, 64, 3000, "bf16", "iid", 33, False, 5),
+    (1, 7, 1, 128, 3000, "bf16", "strat", 128, False, 8),
+    (1, 16, 2, 128, 2500, "bf16", "sys", 256, False, 8),
+    (1, 4, 2, 128, 2049, "f32", "strat", 64, False, 3),
+    (1, 4, 4, 64, 777, "f32", "iid", 1, False, 0),
+    (2, 8, 2, 128, 5000, "bf16", "strat", 64, True, 6),
+    (1, 4, 1, 64, 1500, "bf16", "sys", 1000, True, 2),
+    (1, 8, 2, 128, 2000, "bf16", "strat", 1, False, 4),
+    (1, 8, 2, 128, 2000, "bf16", "sys", 3, False, 4),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"B{c[0]}H{c[1]}kv{c[2]}d{c[3]}n{c[4]}{c[5]}{c[6]}S{c[7]}"
+                                             f"{'T' if c[8] else ''}" for c in SMALL])
+def test_small_cases(case):
+    B, H, Hkv, d, nk, dtype, mode, S, tern, spikes = case
+    log(f"case {case}")
+    q, K, V, _ = workloads.make_inputs(B, H, Hkv, d, nk, dtype=dtype, spikes_per_head=spikes,
+                                       rng_seed=zlib.crc32(repr(case).encode()) & 0xFFFF)
+    for seed in (0, 12345):
+        rep, *_ = compare(q, K, V, S, mode, seed, ternary=tern, dtype=dtype, label=str(case))
+        log(f"  seed {seed}: {rep}")
+
+
+def test_strided_caches():
+    B, H, Hkv, d, nk = 2, 8, 2, 128, 3000
+    log("strided caches")
+    q, K, V, _ = workloads.make_inputs(B, H, Hkv, d, nk + 7, dtype="bf16", spikes_per_head=3, rng_seed=77)
+    # preallocated cache with spare positions: batch stride (nk+7)*Hkv*d, attend to the first nk
+    rep, *_ = compare(q, K, V, 64, "strat", 5, nk=nk, label="spare positions")
+    log(f"  {rep}")
+    # padded positions: an extra KV head slot per position (seq stride (Hkv+1)*d)
+    Kp = torch.zeros((B, nk, Hkv + 1, d), dtype=K.dtype)
+    Vp = torch.zeros_like(Kp)
+    Kp[:, :, :Hkv] = K[:, :nk]
+    Vp[:, :, :Hkv] = V[:, :nk]
+    dev = torch.device("cuda:0")
+    Kd, Vd = Kp.to(dev)[:, :, :Hkv], Vp.to(dev)[:, :, :Hkv]
+    idx = torch.empty((B, H, 64), dtype=torch.int32, device=dev)
+    out = santa.decode(q.to(dev), Kd, Vd, 64, "strat", 5, idx_out=idx)
+    torch.cuda.synchronize()
+    r = oracle.decode(q.float().numpy(), K[:, :nk].float().numpy(), V[:, :nk].float().numpy(), 64, oracle.STRAT, 5)
+    assert np.array_equal(idx.cpu().numpy(), r.idx)
+    assert np.max(np.abs(out.float().cpu().numpy() - r.out)) <= 2e-2
+
+
+def test_workload_2_full_size():
+    w = workloads.make(2)
+    log(f"workload 2 {w.name}: B{w.B} H{w.H}/{w.Hkv} d{w.d} nk{w.nk} {w.mode} S{w.S}")
+    rep, r, out, idx = compare(w.q, w.K, w.V, w.S, w.mode, w.seed, dtype=w.dtype, label=w.name)
+    log(f"  {rep}")
+    assert rep["mismatches"] == 0
+
+
+def test_workload_3_full_size_sweep():
+    w = workloads.make(3)
+    log(f"workload 3 {w.name}: B{w.B} nk{w.nk} sys S in {w.S_sweep}")
+    for i, S in enumerate((64, 256, 1024)):
+        rep, *_ = compare(w.q, w.K, w.V, S, w.mode, w.seed, dtype=w.dtype, want_prob=(i == 0),
+                          label=f"{w.name} S={S}")
+        log(f"  S={S}: {rep}")
+
+
+def test_workload_3_reduced_nk_all_S():
+    w = workloads.make(3, nk=4096)
+    for S in w.S_sweep:
+        log(f"workload 3 nk=4096 S={S}")
+        rep, *_ = compare(w.q, w.K, w.V, S, w.mode, w.seed, dtype=w.dtype, label=f"batched nk4096 S={S}")
+        log(f"  {rep}")
+
+
+def test_workload_4_full_size():
+    w = workloads.make(4)
+    log(f"workload 4 {w.name}: G{w.G} nk{w.nk} {w.mode} S{w.S}")
+    rep, *_ = compare(w.q, w.K, w.V, w.S, w.mode, w.seed, dtype=w.dtype, label=w.name)
+    log(f"  {rep}")
+
+
+def test_workload_5_full_size_ternary():
+    w = workloads.make(5)
+    log(f"workload 5 {w.name}: B{w.B} nk{w.nk} ternary {w.mode} S{w.S}")
+    rep, *_ = compare(w.q, w.K, w.V, w.S, w.mode, w.seed, ternary=True, dtype=w.dtype, label=w.name)
+    log(f"  {rep}")
+
+
+def test_one_hot_and_uniform_attention():
+    log("one-hot and uniform attention")
+    dev = torch.device("cuda:0")
+    nk, d = 3000, 128
+    q, K, V, _ = workloads.make_inputs(1, 4, 1, d, nk, dtype="bf16", rng_seed=3)
+    q[0, 1:] = q[0, 0]
+    K = K * 0.01
+    K[0, 1234, 0] = q[0, 0] * 128.0  # logit ~ 128|q|^2/sqrt(d): every other key underflows to 0
+    for mode in ("iid", "strat", "sys"):
+        idx = torch.empty((1, 4, 32), dtype=torch.int32, device=dev)
+        out = santa.decode(q.to(dev), K.to(dev), V.to(dev), 32, mode, 9, idx_out=idx)
+        torch.cuda.synchronize()
+        assert torch.all(idx == 1234)
+        assert torch.equal(out.cpu()[0], V[0, 1234, 0].unsqueeze(0).expand(4, d))
+    # uniform attention (all logits 0), systematic with S = 2 nk: every key exactly twice
+    nk = 300
+    gen = torch.Generator().manual_seed(0)
+    K0 = torch.zeros((1, nk, 1, d), dtype=torch.bfloat16)
+    V0 = torch.randn((1, nk, 1, d), generator=gen).to(torch.bfloat16)
+    q0 = torch.randn((1, 2, d), generator=gen).to(torch.bfloat16)
+    idx = torch.empty((1, 2, 2 * nk), dtype=torch.int32, device=dev)
+    out = santa.decode(q0.to(dev), K0.to(dev), V0.to(dev), 2 * nk, "sys", 4, idx_out=idx)
+    torch.cuda.synchronize()
+    for h in range(2):
+        assert np.array_equal(np.bincount(idx[0, h].cpu().numpy(), minlength=nk), np.full(nk, 2))
+    mean = oracle.round_to_bf16(V0[0, :, 0].double().numpy().mean(axis=0))
+    assert np.array_equal(out.float().cpu().numpy()[0, 0], mean)
+
+
+def test_strat_equals_iid_at_S1_and_determinism():
+    log("S=1 consistency and determinism")
+    dev = torch.device("cuda:0")
+    q, K, V, _ = workloads.make_inputs(1, 8, 2, 128, 5000, dtype="bf16", spikes_per_head=4, rng_seed=21)
+    qd, Kd, Vd = q.to(dev), K.to(dev), V.to(dev)
+    i1 = torch.empty((1, 8, 1), dtype=torch.int32, device=dev)
+    i2 = torch.empty_like(i1)
+    santa.decode(qd, Kd, Vd, 1, "iid", 77, idx_out=i1)
+    santa.decode(qd, Kd, Vd, 1, "strat", 77, idx_out=i2)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    a = santa.decode(qd, Kd, Vd, 256, "strat", 5)
+    b = santa.decode(qd, Kd, Vd, 256, "strat", 5)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_simple_entry_point_matches_ex():
+    log("santa_decode vs santa_decode_ex")
+    dev = torch.device("cuda:0")
+    q, K, V, _ = workloads.make_inputs(1, 8, 2, 128, 4000, dtype="bf16", spikes_per_head=4, rng_seed=31)
+    qd, Kd, Vd = q.to(dev), K.to(dev), V.to(dev)
+    a = santa.decode(qd, Kd, Vd, 128, "sys", 3)
+    b = santa.decode_simple(qd, Kd, Vd, 128, "sys", 3)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_dense_baseline_matches_oracle():
+    log("dense baseline")
+    dev = torch.device("cuda:0")
+    for (B, H, Hkv, d, nk, dtype) in [(1, 32, 8, 128, 32768, "bf16"), (2, 7, 1, 64, 1500, "bf16"),
+                                      (1, 4, 2, 128, 1000, "f32")]:
+        q, K, V, _ = workloads.make_inputs(B, H, Hkv, d, nk, dtype=dtype, spikes_per_head=4, rng_seed=nk)
+        out = santa.dense_decode(q.to(dev), K.to(dev), V.to(dev))
+        torch.cuda.synchronize()
+        mu, mu_r = oracle.dense(q.float().numpy(), K.float().numpy(), V.float().numpy(), out_dtype=dtype)
+        err = np.max(np.abs(out.float().cpu().numpy() - mu))
+        log(f"  dense B{B} H{H}/{Hkv} d{d} nk{nk} {dtype}: max abs {err:.3g}")
+        assert err <= (1e-2 if dtype == "bf16" else 1e-4)
+
+
+def test_gpu_estimator_unbiased_4096_seeds():
+    """Mean of the GPU estimate over 4096 seeds is within 3 sigma of dense AV (workload 1, i.i.d.)."""
+    log("GPU unbiasedness over 4096 seeds")
+    w = workloads.make(1)
+    dev = torch.device("cuda:0")
+    qd, Kd, Vd = w.q.to(dev), w.K.to(dev), w.V.to(dev)
+    ws = torch.empty(santa.workspace_bytes(1, w.nk, 1, 1, w.d, w.S), dtype=torch.uint8, device=dev)
+    outs = torch.empty((4096, w.d), dtype=torch.float32, device=dev)
+    for seed in range(4096):
+        santa.decode(qd, Kd, Vd, w.S, "iid", seed, out=outs[seed].view(1, 1, w.d), workspace=ws)
+    torch.cuda.synchronize()
+    ests = outs.double().cpu().numpy()
+    qn, Kn, Vn = w.numpy_inputs()
+    Kf, Vf = Kn[0, :, 0].astype(np.float64), Vn[0, :, 0].astype(np.float64)
+    p, _, _ = oracle.softmax(oracle.scores_exact(qn[0, 0], Kf))
+    mu = p @ Vf
+    vt = oracle.var_trace_iid(p, Vf, w.S)
+    assert np.linalg.norm(ests.mean(axis=0) - mu) <= 3 * np.sqrt(vt / 4096)
