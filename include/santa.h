@@ -46,7 +46,7 @@ extern "C" {
 /* status codes */
 #define SANTA_OK 0
 #define SANTA_ERR_INVALID_ARG 1     /* null pointer, heads % kv_heads != 0, S < 1, nk < 1, bad mode bits ... */
-#define SANTA_ERR_UNSUPPORTED 2     /* d not in {64, 128}, dtype, sizes beyond the kernels' limits */
+#define SANTA_ERR_UNSUPPORTED 2     /* d not in {64, 128}, dtype, G > 8, nk > 2^20, S > 65535 */
 #define SANTA_ERR_WORKSPACE 3       /* workspace_bytes smaller than santa_workspace_bytes() */
 #define SANTA_ERR_HIP 4             /* a HIP runtime call or launch failed (see santa_last_error) */
 
@@ -87,26 +87,33 @@ typedef struct santa_args {
   int32_t reserved0;
   uint64_t seed;
   void* stream;              /* hipStream_t, NULL = default stream */
-  void* workspace;           /* device scratch of at least santa_workspace_bytes() bytes */
+  void* workspace;           /* device scratch of at least santa_workspace_bytes() bytes; zero-filled before
+                                its first use (its leading counters must start at zero; every completed
+                                call leaves them zero, so it can be reused by later, non-overlapping calls) */
   size_t workspace_bytes;
   /* optional debug outputs; NULL to skip */
   int32_t* idx_out;          /* device [batch, heads, S]: sampled key index of each point, in point order */
   double* prob_out;          /* device [batch, heads, nk]: softmax probabilities */
   santa_stats* stats_out;    /* host; the call synchronises the stream to fill it */
-  float* stage_ms;           /* host float[4]: per-kernel GPU time (events); synchronises the stream */
+  float* stage_ms;           /* host float[4]: GPU time of [score, chunk CDF + resolve, gather, whole call]
+                                from events between the launches; synchronises the stream */
 } santa_args;
 
 /*
  * santa_decode — one SANTA / S²ANTA decode step in its simplest form: batch 1, bf16 q/K/V/out,
- * contiguous [nk, kv_heads, d] caches, the default stream, and a workspace the library allocates on
- * first use and keeps (grow-only) until santa_release(). Returns a status code.
+ * contiguous [nk, kv_heads, d] caches, the default stream, and a zero-filled workspace the library
+ * allocates on first use and keeps (grow-only, per device) until santa_release(). Calls on one device
+ * share that workspace and must not overlap. Returns a status code.
  */
 int santa_decode(const void* q, const void* K, const void* V, int64_t nk, int heads, int kv_heads, int d, int S,
                  int mode, uint64_t seed, void* out);
 
 /*
- * santa_decode_ex — the full form. Caller-owned workspace (`workspace`, `workspace_bytes`); never
- * allocates device memory. Launches the score, sampling and gather kernels on `stream`.
+ * santa_decode_ex — the full form. Caller-owned workspace (`workspace`, `workspace_bytes`, zero-filled
+ * before first use); never allocates device memory. Launches four kernels on `stream`: the split-K score
+ * pass, the chunk CDF per KV group, the sampling pass per chunk (which lists each group's distinct
+ * sampled rows with per-head counts) and the gather per KV group. Calls sharing one workspace must not
+ * overlap.
  */
 int santa_decode_ex(const santa_args* a);
 

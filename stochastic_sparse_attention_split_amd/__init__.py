@@ -130,6 +130,12 @@ def workspace_bytes(B: int, nk: int, H: int, Hkv: int, d: int, S: int, mode=STRA
     return int(lib().santa_workspace_bytes(B, nk, H, Hkv, d, S, _mode_code(mode, False)))
 
 
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled workspace for decode(): the library's counters must start at zero; every completed
+    call leaves them at zero again, so a workspace can be reused across calls (not concurrently)."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
 def dense_workspace_bytes(B: int, nk: int, H: int, Hkv: int, d: int) -> int:
     return int(lib().santa_dense_workspace_bytes(B, nk, H, Hkv, d))
 
@@ -164,7 +170,8 @@ def decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="stra
     """One SANTA / S²ANTA decode step through santa_decode_ex.
 
     Returns out, or (out, info) when stats or stage_ms is requested (info holds the stats fields and the
-    per-kernel milliseconds [score, sample, gather, total]).
+    per-kernel milliseconds [score, chunk CDF + resolve, gather, total]). A caller-provided workspace must have been
+    zero-filled before its first use (see new_workspace).
     """
     if out is None:
         out = torch.empty_like(q)
@@ -175,7 +182,7 @@ def decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="stra
     a.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
     need = int(lib().santa_workspace_bytes(a.batch, a.nk, a.heads, a.kv_heads, a.d, a.S, a.mode))
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = new_workspace(need, q.device)
     a.workspace = workspace.data_ptr()
     a.workspace_bytes = workspace.numel() * workspace.element_size()
     if idx_out is not None:

@@ -56,6 +56,15 @@ constexpr uint32_t TAG_SYS = 1;        // systematic offset (m = 0)
 constexpr uint32_t TAG_BERNOULLI = 2;  // ternary-query element m (+256 n for Bernoulli sample n)
 
 // ---------------------------------------------------------------------------------------------
+// 16-byte streaming load that does not allocate in the caches (K and V are read once per step; a
+// non-temporal load also avoids evicting dirty lines from the Infinity Cache)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline uint4 load_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ---------------------------------------------------------------------------------------------
 // element conversions
 
 // bf16 pair packed in a 32-bit word -> two floats (exact: bf16 is the top half of an fp32)
@@ -114,7 +123,57 @@ struct Piece<false> {
 };
 
 // ---------------------------------------------------------------------------------------------
+// fp64 wavefront operations with DPP (row shifts within 16-lane rows, then row broadcasts 15 / 31):
+// six dependent VALU steps instead of LDS-latency lane permutes.
+template <int CTRL, int ROW_MASK>
+__device__ inline double dpp_f64(double old, double src) {
+  const long long o = __double_as_longlong(old), s = __double_as_longlong(src);
+  const int lo = __builtin_amdgcn_update_dpp((int)o, (int)s, CTRL, ROW_MASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(o >> 32), (int)(s >> 32), CTRL, ROW_MASK, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// inclusive prefix sum over the 64 lanes (lane i gets the sum of lanes 0..i)
+__device__ inline double wave_incl_scan_dpp(double v) {
+  v += dpp_f64<0x111, 0xf>(0.0, v);  // row_shr:1
+  v += dpp_f64<0x112, 0xf>(0.0, v);  // row_shr:2
+  v += dpp_f64<0x114, 0xf>(0.0, v);  // row_shr:4
+  v += dpp_f64<0x118, 0xf>(0.0, v);  // row_shr:8
+  v += dpp_f64<0x142, 0xa>(0.0, v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f64<0x143, 0xc>(0.0, v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// running maximum over the lanes; lane 63 holds the wave maximum
+__device__ inline double wave_incl_max_dpp(double v) {
+  const double ninf = -INFINITY;
+  v = fmax(v, dpp_f64<0x111, 0xf>(ninf, v));
+  v = fmax(v, dpp_f64<0x112, 0xf>(ninf, v));
+  v = fmax(v, dpp_f64<0x114, 0xf>(ninf, v));
+  v = fmax(v, dpp_f64<0x118, 0xf>(ninf, v));
+  v = fmax(v, dpp_f64<0x142, 0xa>(ninf, v));
+  v = fmax(v, dpp_f64<0x143, 0xc>(ninf, v));
+  return v;
+}
+
+// value of lane `l` (wave-uniform), fp64
+__device__ inline double readlane_f64(double v, int l) {
+  const long long x = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)x, l);
+  const int hi = __builtin_amdgcn_readlane((int)(x >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// ---------------------------------------------------------------------------------------------
 // problem description passed to kernels
+
+// one distinct sampled V row of a (KV head, sequence) group: key index and 16-bit per-head counts
+struct RowRecord {
+  int32_t key;
+  uint32_t counts[4];  // head g in the low (g even) or high (g odd) half of counts[g / 2]
+  int32_t pad[3];
+};
+static_assert(sizeof(RowRecord) == 32, "two 16-byte loads per record");
 
 struct Problem {
   const void* q;
@@ -132,10 +191,16 @@ struct Problem {
   uint64_t seed;
   double scale;          // 1/sqrt(d), formed on the host in fp64
   int T;                 // chunks per sequence
+  int score_blocks_per_group;  // score blocks per (KV head, sequence); each loops over chunks
   // workspace
+  int32_t* counters;     // [B*Hkv] row-list lengths; zero between calls
   double* stash;         // [B, H, nk] in-chunk inclusive prefix of exp(s - m_t)
   double* cmax;          // [B, H, T] chunk max m_t
   double* csum;          // [B, H, T] chunk sum-exp l_t
+  double* cdf;           // [B, H, T+1] exclusive prefix of W_t = l_t exp(m_t - m*); cdf[T] = Z
+  double* cscale;        // [B, H, T] exp(m_t - m*)
+  int32_t* lastpos;      // [B, H] last chunk with W_t > 0
+  RowRecord* rows;       // [B*Hkv][G*S] distinct sampled rows per group
   int32_t* idx;          // [B, H, S]
   int32_t* unique;       // [B, Hkv]
   double* prob;          // optional [B, H, nk]

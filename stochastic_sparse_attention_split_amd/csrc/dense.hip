@@ -76,7 +76,7 @@ __global__ __launch_bounds__(THREADS) void dense_partial_kernel(DenseProblem p) 
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
       const int r = rg + (k0 + k) * NRG;
-      w[k] = r < len ? *((const uint4*)(kb + r * rs) + pc) : make_uint4(0, 0, 0, 0);
+      w[k] = load_stream16((const uint4*)(kb + (r < len ? r : 0) * rs) + pc);  // tail rows masked below
     }
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(THREADS) void dense_partial_kernel(DenseProblem p) 
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
       const int r = rg + (k0 + k) * NRG;
-      w[k] = r < len ? *((const uint4*)(vb + r * rs) + pc) : make_uint4(0, 0, 0, 0);
+      w[k] = load_stream16((const uint4*)(vb + (r < len ? r : 0) * rs) + pc);  // tail rows masked below
     }
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
@@ -177,21 +177,57 @@ __global__ __launch_bounds__(THREADS) void dense_partial_kernel(DenseProblem p) 
   }
 }
 
+// merge: block per (head, sequence); chunk weights f_t = exp(m_t - m*) in LDS, then every thread sums
+// a strided slice of the chunks for one output element, 8 loads in flight
+constexpr int MERGE_THREADS = 256;
 template <int D, bool BF16>
-__global__ __launch_bounds__(128) void dense_merge_kernel(DenseProblem p) {
+__global__ __launch_bounds__(MERGE_THREADS) void dense_merge_kernel(DenseProblem p) {
+  __shared__ float f[MAX_CHUNKS * CHUNK / DENSE_CHUNK];
+  __shared__ float red[MERGE_THREADS / 64];
+  __shared__ float osum[MERGE_THREADS / D][D];
   const int h = blockIdx.x, b = blockIdx.y;
-  const float* src = p.part + ((int64_t)b * p.H + h) * p.Td * (D + 2);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Td = p.Td;
+  const float* src = p.part + ((int64_t)b * p.H + h) * Td * (D + 2);
   float m = -INFINITY;
-  for (int t = 0; t < p.Td; ++t) m = fmaxf(m, src[t * (D + 2) + D]);
-  for (int e = threadIdx.x; e < D; e += blockDim.x) {
-    float o = 0.f, l = 0.f;
-    for (int t = 0; t < p.Td; ++t) {
-      const float f = __expf(src[t * (D + 2) + D] - m);
-      o += f * src[t * (D + 2) + e];
-      l += f * src[t * (D + 2) + D + 1];
+  for (int t = tid; t < Td; t += MERGE_THREADS) m = fmaxf(m, src[t * (D + 2) + D]);
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  float ms = red[0];
+  for (int w = 1; w < MERGE_THREADS / 64; ++w) ms = fmaxf(ms, red[w]);
+  __syncthreads();
+  float l = 0.f;
+  for (int t = tid; t < Td; t += MERGE_THREADS) {
+    const float ft = __expf(src[t * (D + 2) + D] - ms);
+    f[t] = ft;
+    l += ft * src[t * (D + 2) + D + 1];
+  }
+  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+  if (lane == 0) red[wave] = l;
+  __syncthreads();
+  float lsum = 0.f;
+  for (int w = 0; w < MERGE_THREADS / 64; ++w) lsum += red[w];
+  constexpr int SL = MERGE_THREADS / D;  // chunk slices
+  const int e = tid % D, sl = tid / D;
+  float o = 0.f;
+  for (int t0 = sl; t0 < Td; t0 += SL * 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int t = t0 + k * SL;
+      v[k] = t < Td ? f[t] * src[t * (D + 2) + e] : 0.f;
     }
-    const float r = o / l;
-    const int64_t oi = ((int64_t)b * p.H + h) * D + e;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o += v[k];
+  }
+  osum[sl][e] = o;
+  __syncthreads();
+  if (tid < D) {
+    float r = 0.f;
+    for (int k = 0; k < SL; ++k) r += osum[k][tid];
+    r /= lsum;
+    const int64_t oi = ((int64_t)b * p.H + h) * D + tid;
     if (BF16)
       ((uint16_t*)p.out)[oi] = f32_to_bf16_rne(r);
     else
@@ -212,7 +248,7 @@ hipError_t launch_dense_dt(const DenseProblem& p, hipStream_t st) {
     dense_partial_kernel<D, BF16, 8><<<grid, THREADS, 0, st>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dense_merge_kernel<D, BF16><<<dim3(p.H, p.B), 128, 0, st>>>(p);
+  dense_merge_kernel<D, BF16><<<dim3(p.H, p.B), MERGE_THREADS, 0, st>>>(p);
   return hipGetLastError();
 }
 

@@ -8,8 +8,10 @@
 namespace santa {
 
 hipError_t launch_score(const Problem& p, hipStream_t st);     // score.hip
-hipError_t launch_sample(const Problem& p, hipStream_t st);    // sample.hip
-hipError_t launch_gather(const Problem& p, hipStream_t st);    // gather.hip
+int score_blocks_per_cu(int d, bool bf16, int G);              // resident score blocks per CU (LDS)
+hipError_t launch_chunk_cdf(const Problem& p, hipStream_t st); // score.hip
+hipError_t launch_resolve(const Problem& p, hipStream_t st);   // resolve.hip
+hipError_t launch_gather(const Problem& p, hipStream_t st);    // resolve.hip
 
 // dense baseline (dense.hip): partials [B, H, Td, d + 2] fp32 then a merge
 struct DenseProblem {
@@ -26,8 +28,5 @@ struct DenseProblem {
 };
 constexpr int DENSE_CHUNK = 512;
 hipError_t launch_dense(const DenseProblem& p, hipStream_t st);
-
-// LDS bytes the gather kernel needs for a group of G heads with S samples each
-size_t gather_lds_bytes(int G, int S);
 
 }  // namespace santa

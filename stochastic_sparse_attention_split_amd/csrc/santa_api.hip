@@ -1,5 +1,5 @@
 // C ABI of libsanta.so: argument validation (before any HIP call), workspace layout, and the launch
-// sequence score -> sample -> gather on the caller's stream. See include/santa.h for the contract.
+// sequence score -> chunk CDF -> resolve -> gather on the caller's stream. See include/santa.h.
 
 #include <cmath>
 #include <cstdarg>
@@ -35,26 +35,32 @@ int hip_fail(hipError_t e, const char* what) {
 
 constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
-constexpr size_t LDS_LIMIT = 160 * 1024 - 1024;  // dynamic LDS left beside the kernels' static LDS
 
 struct Layout {
-  size_t stash, cmax, csum, idx, unique, total;
+  size_t counters, stash, cmax, csum, cdf, cscale, lastpos, rows, idx, unique, total;
 };
 
+// counters first: the only part of the workspace that must be zero before its first use
 Layout layout(int64_t B, int64_t nk, int64_t H, int64_t Hkv, int64_t S) {
   const int64_t T = (nk + CHUNK - 1) / CHUNK;
+  const int64_t G = H / Hkv;
   Layout L;
   size_t off = 0;
-  L.stash = off;
-  off = align_up(off + (size_t)(B * H * nk) * sizeof(double));
-  L.cmax = off;
-  off = align_up(off + (size_t)(B * H * T) * sizeof(double));
-  L.csum = off;
-  off = align_up(off + (size_t)(B * H * T) * sizeof(double));
-  L.idx = off;
-  off = align_up(off + (size_t)(B * H * S) * sizeof(int32_t));
-  L.unique = off;
-  off = align_up(off + (size_t)(B * Hkv) * sizeof(int32_t));
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.counters = take((size_t)(B * Hkv) * sizeof(int32_t));
+  L.stash = take((size_t)(B * H * nk) * sizeof(double));
+  L.cmax = take((size_t)(B * H * T) * sizeof(double));
+  L.csum = take((size_t)(B * H * T) * sizeof(double));
+  L.cdf = take((size_t)(B * H * (T + 1)) * sizeof(double));
+  L.cscale = take((size_t)(B * H * T) * sizeof(double));
+  L.lastpos = take((size_t)(B * H) * sizeof(int32_t));
+  L.rows = take((size_t)(B * Hkv * G * S) * sizeof(RowRecord));
+  L.idx = take((size_t)(B * H * S) * sizeof(int32_t));
+  L.unique = take((size_t)(B * Hkv) * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -98,10 +104,30 @@ int validate_sampled(const santa_args* a, int64_t* seq, int64_t* bstride) {
   if (base > SANTA_SYS || base < 0 || (flags & ~SANTA_TERNARY_Q))
     return fail(SANTA_ERR_INVALID_ARG, "mode 0x%x has unknown bits", (unsigned)a->mode);
   if (a->S > 65535) return fail(SANTA_ERR_UNSUPPORTED, "S %d exceeds 65535", a->S);
-  const int G = a->heads / a->kv_heads;
-  if (gather_lds_bytes(G, a->S) > LDS_LIMIT)
-    return fail(SANTA_ERR_UNSUPPORTED, "G*S = %d samples per KV group exceed the gather kernel's LDS table", G * a->S);
   return SANTA_OK;
+}
+
+// compute units of the current device (queried once per device)
+int device_cus() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// as many score blocks as fit on the device at once, spread over the (KV head, sequence) groups
+int score_blocks_per_group(int groups, int T, int per_cu) {
+  const int target = per_cu * device_cus();
+  int per = (target + groups - 1) / groups;
+  return per < 1 ? 1 : (per > T ? T : per);
 }
 
 struct Events {
@@ -155,9 +181,15 @@ int santa_decode_ex(const santa_args* a) {
   p.seed = a->seed;
   p.scale = 1.0 / std::sqrt((double)a->d);
   p.T = (int)((a->nk + CHUNK - 1) / CHUNK);
+  p.score_blocks_per_group = score_blocks_per_group(p.B * p.Hkv, p.T, score_blocks_per_cu(p.d, p.bf16, p.G));
+  p.counters = (int32_t*)(ws + L.counters);
   p.stash = (double*)(ws + L.stash);
   p.cmax = (double*)(ws + L.cmax);
   p.csum = (double*)(ws + L.csum);
+  p.cdf = (double*)(ws + L.cdf);
+  p.cscale = (double*)(ws + L.cscale);
+  p.lastpos = (int32_t*)(ws + L.lastpos);
+  p.rows = (RowRecord*)(ws + L.rows);
   p.idx = a->idx_out ? a->idx_out : (int32_t*)(ws + L.idx);
   p.unique = (int32_t*)(ws + L.unique);
   p.prob = a->prob_out;
@@ -176,7 +208,8 @@ int santa_decode_ex(const santa_args* a) {
   (void)hipGetLastError();  // start from a clean error state
   if ((e = launch_score(p, stream)) != hipSuccess) return hip_fail(e, "score kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  if ((e = launch_sample(p, stream)) != hipSuccess) return hip_fail(e, "sample kernel launch");
+  if ((e = launch_chunk_cdf(p, stream)) != hipSuccess) return hip_fail(e, "chunk CDF kernel launch");
+  if ((e = launch_resolve(p, stream)) != hipSuccess) return hip_fail(e, "resolve kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if ((e = launch_gather(p, stream)) != hipSuccess) return hip_fail(e, "gather kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -191,7 +224,7 @@ int santa_decode_ex(const santa_args* a) {
     for (int32_t x : u) U += x;
     const int64_t esz = p.bf16 ? 2 : 4;
     santa_stats* s = a->stats_out;
-    s->launches = 3;
+    s->launches = 4;
     s->bytes_k = (int64_t)a->batch * a->nk * a->kv_heads * a->d * esz;
     s->bytes_v = U * a->d * esz;
     s->bytes_qo = 2 * (int64_t)a->batch * a->heads * a->d * esz;
@@ -258,6 +291,7 @@ int santa_decode(const void* q, const void* K, const void* V, int64_t nk, int he
       w.bytes = 0;
     }
     if ((e = hipMalloc(&w.ptr, need)) != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
+    if ((e = hipMemset(w.ptr, 0, need)) != hipSuccess) return hip_fail(e, "hipMemset(workspace)");
     w.bytes = need;
   }
   a.workspace = w.ptr;

@@ -1,19 +1,24 @@
-// Split-K score pass: one block per (chunk of CHUNK keys, KV head, sequence).
+// Split-K score pass: blocks pinned to one (KV head, sequence) group, each looping over a strided set
+// of CHUNK-key chunks of that group.
 //
 // "Stochastic Sparse Attention for Memory-Bound Inference", Appendix O, Algorithm 3 (pass-1 tile
 // statistics with the optional stash) and Section 3.2 ("Pass 1"): for every query head h of the GQA
-// group, s_{h,n} = q_h . K_n / sqrt(dk) (Eq. 1), chunk max m_{h,t}, and the in-chunk exponentials
+// group, s_{h,n} = q_h . K_n / sqrt(dk) (Eq. 1), the chunk max m_{h,t}, and the in-chunk exponentials
 // exp(s_{h,n} - m_{h,t}). This pass stores their in-chunk inclusive prefix sums (the chunk's CDF up to
 // the chunk's own scale) and l_{h,t} = the chunk total, which is what the sampler's inverse CDF needs.
 //
 // MI355X design:
-//   * K is read once, 16 bytes per lane per load, every row shared by the G heads of its group.
-//   * The dot products run on the fp64 matrix cores (v_mfma_f64_4x4x4_4b: 4 blocks of 4 keys x 4 dims
-//     x 4 heads), so a 16-key group needs no cross-lane reduction: lane l holds key (l & 15) at dim
-//     slot (l >> 4) for A, head (l & 3) at dim slot (l >> 4) for B, and receives the score of key
-//     4*((l >> 2) & 3) + (l >> 4), head (l & 3). Products of bf16 (or fp32) inputs are exact in fp64
-//     and accumulate in fp64, which the sampler's index parity needs.
-//   * exp, max and the prefix scan are fp64 wavefront operations on 256 keys per block.
+//   * K is streamed once with non-temporal 16-byte loads in full-row order (16 lanes cover a 256-byte
+//     row), the next chunk's loads in flight while the current chunk is computed. The current chunk
+//     sits in a padded LDS tile (row stride + 16 bytes), from which the matrix-core layout is read
+//     without bank conflicts.
+//   * Dot products run on the fp64 matrix cores (v_mfma_f64_4x4x4_4b: 4 blocks of 4 keys x 4 dims x
+//     4 heads): lane l supplies key (l & 15) at dim slot (l >> 4) for A and head (l & 3) at dim slot
+//     (l >> 4) for B, and receives the score of key 4*((l >> 2) & 3) + (l >> 4), head (l & 3); no
+//     cross-lane reduction. Products of bf16 (or fp32) inputs are exact in fp64 and accumulate in fp64,
+//     which the sampler's index parity needs. Four independent accumulation chains per wave.
+//   * Softmax bookkeeping: a wave owns a head, a lane owns 4 consecutive keys: local max / exp /
+//     prefix, then DPP wavefront max and scan (fp64).
 //   * With the Bernoulli ternary query (Section 5, Eq. 5; Appendix C, Eqs. 8-9) the B operand holds
 //     qhat in {-1, 0, +1} and the score is (qhat . K) * norm * (1/sqrt(dk)).
 
@@ -26,61 +31,139 @@ namespace {
 
 constexpr int THREADS = 256;   // 4 waves; 64 keys per wave, 16 keys per MFMA group
 constexpr int GROUPS_PER_WAVE = 4;
+static_assert(THREADS / 64 * GROUPS_PER_WAVE * 16 == CHUNK, "a block covers one chunk per iteration");
+static_assert(4 * 64 == CHUNK, "a wave covers one chunk with 4 keys per lane in the softmax step");
 
-__device__ inline double wave_max(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-__device__ inline double wave_incl_scan(double v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
+// element e of a 16-byte piece, widened exactly to fp64
+template <bool BF16>
+__device__ inline double piece_elem(const uint4& w, int e) {
+  if constexpr (BF16) {
+    const uint32_t x = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
+    return (double)((e & 1) ? bf16_hi(x) : bf16_lo(x));
+  } else {
+    const uint32_t x = e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
+    return (double)__uint_as_float(x);
   }
-  return v;
 }
 
-// NQ = number of 4-head quads (1: G <= 4, 2: G <= 8)
-template <int D, bool BF16, int NQ>
-__global__ __launch_bounds__(THREADS) void score_kernel(Problem p) {
-  using P = Piece<BF16>;
-  constexpr int EPL = P::EPL;
-  constexpr int NPIECE = D / EPL;     // 16-byte pieces per row
-  constexpr int PP = NPIECE / 4;      // pieces per lane per row (lane takes pieces 4*pp + slot)
+template <int D, bool BF16>
+struct Geo {
+  static constexpr int ESZ = BF16 ? 2 : 4;
+  static constexpr int ROWB = D * ESZ;              // bytes per K row
+  static constexpr int NPR = ROWB / 16;             // 16-byte pieces per row
+  static constexpr int RSTRIDE = ROWB + 16;         // padded LDS row stride (conflict-free MFMA reads)
+  static constexpr int NLD = CHUNK * NPR / THREADS; // 16-byte loads per thread per chunk
+  static constexpr int RPI = THREADS / NPR;         // rows covered by one block-wide load instruction
+  static constexpr int EPL = 16 / ESZ;              // elements per piece
+  static constexpr int PP = NPR / 4;                // pieces per lane per row in the MFMA layout
+  static constexpr int LDS_K = CHUNK * RSTRIDE;
+};
+
+// full-row loads of chunk rows [n0, n0+len): load i covers row i*RPI + tid/NPR, piece tid%NPR; rows past
+// the end re-read row n0 (always valid) so every load is unconditional; those keys are masked later
+template <int D, bool BF16>
+__device__ inline void load_rows(uint4* r, const char* kbase, int64_t seq_bytes, int64_t n0, int len, int tid) {
+  using Gm = Geo<D, BF16>;
+  const int piece = tid % Gm::NPR, row0 = tid / Gm::NPR;
+#pragma unroll
+  for (int i = 0; i < Gm::NLD; ++i) {
+    const int row = i * Gm::RPI + row0;
+    r[i] = load_stream16(kbase + (n0 + (row < len ? row : 0)) * seq_bytes + piece * 16);
+  }
+}
+
+template <int D, bool BF16>
+__device__ inline void store_rows(unsigned char* ks, const uint4* r, int tid) {
+  using Gm = Geo<D, BF16>;
+  const int piece = tid % Gm::NPR, row0 = tid / Gm::NPR;
+#pragma unroll
+  for (int i = 0; i < Gm::NLD; ++i) *(uint4*)(ks + (i * Gm::RPI + row0) * Gm::RSTRIDE + piece * 16) = r[i];
+}
+
+// Chunk CDF (Appendix O, Algorithm 4: m* = max_t m_t, W_t = l_t exp(m_t - m*), Z = sum_t W_t) of the
+// heads of one (KV head, sequence) group, one wave per head (waves take heads wave, wave + 4): lane l owns
+// a contiguous run of chunks; the prefix is exclusive, then made monotone by a running maximum so that
+// the chunks' intervals [cdf_t, cdf_{t+1}) partition [0, Z) exactly. cdf[T] = Z. One block per group.
+__global__ __launch_bounds__(THREADS) void chunk_cdf_kernel(Problem p) {
+  const int kv = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h0 = kv * p.G;
+  const int T = p.T;
+  const int per = (T + 63) / 64;
+  const int t0 = min(T, lane * per), t1 = min(T, t0 + per);
+  for (int g = wave; g < p.G; g += THREADS / 64) {
+    const int64_t bh = (int64_t)b * p.H + h0 + g;
+    const double* cm = p.cmax + bh * T;
+    const double* cs = p.csum + bh * T;
+    double* cdf = p.cdf + bh * (T + 1);
+    double* csc = p.cscale + bh * T;
+    double mx = -INFINITY;
+    for (int t = t0; t < t1; ++t) mx = fmax(mx, cm[t]);
+    const double ms = readlane_f64(wave_incl_max_dpp(mx), 63);
+    double run = 0.0;
+    int lp = -1;
+    for (int t = t0; t < t1; ++t) {
+      const double f = exp(cm[t] - ms);
+      const double w = cs[t] * f;
+      csc[t] = f;
+      cdf[t] = run;  // local exclusive prefix, offset below
+      run += w;
+      if (w > 0.0) lp = t;
+    }
+    const double incl = wave_incl_scan_dpp(run);
+    double excl = __shfl_up(incl, 1, 64);
+    if (lane == 0) excl = 0.0;
+    double lmax = 0.0;
+    for (int t = t0; t < t1; ++t) {
+      const double c = fmax(excl + cdf[t], lmax);
+      cdf[t] = c;
+      lmax = c;
+    }
+    // running maximum across lanes: lane l's values are raised to the maximum of all earlier lanes
+    const double pmax = wave_incl_max_dpp(t1 > t0 ? lmax : 0.0);
+    double before = __shfl_up(pmax, 1, 64);
+    if (lane == 0) before = 0.0;
+    for (int t = t0; t < t1; ++t) cdf[t] = fmax(cdf[t], before);
+    const double Z = readlane_f64(incl, 63);
+    const double top = readlane_f64(pmax, 63);
+    if (lane == 0) cdf[T] = fmax(Z, top);
+    const double lpd = readlane_f64(wave_incl_max_dpp((double)lp), 63);
+    if (lane == 0) p.lastpos[bh] = (int32_t)lpd;
+  }
+}
+
+// NQ = number of 4-head quads (1: G <= 4, 2: G <= 8); MINB = resident blocks per CU the LDS allows
+template <int D, bool BF16, int NQ, int MINB>
+__global__ __launch_bounds__(THREADS, MINB) void score_kernel(Problem p) {
+  using Gm = Geo<D, BF16>;
+  constexpr int EPL = Gm::EPL, PP = Gm::PP;
   constexpr int HMAX = 4 * NQ;
+  static_assert(CHUNK >= D + 2, "the query staging aliases the score tile");
 
+  __shared__ __align__(16) unsigned char ks[Gm::LDS_K];
   __shared__ double sc[HMAX][CHUNK];
-  __shared__ double qe[HMAX][D];
-  __shared__ double red[THREADS / 64][HMAX];
   __shared__ double hnorm[HMAX];
+  double (*qe)[D + 2] = reinterpret_cast<double (*)[D + 2]>(&sc[0][0]);  // prologue only
 
-  const int t = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int kv = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = p.G;
   const int h0 = kv * G;
-  const int64_t n0 = (int64_t)t * CHUNK;
-  const int len = (int)((p.nk - n0) < CHUNK ? (p.nk - n0) : CHUNK);
+  const int T = p.T;
+  const int step = gridDim.x;
+  int t = blockIdx.x;
+  if (t >= T) return;
 
-  // ---- issue the K loads first: lane (slot = lane >> 4, key = lane & 15) of each 16-key group
-  const int slot = lane >> 4;
-  const char* kbase = (const char*)p.K;
-  const size_t esz = BF16 ? 2 : 4;
-  uint4 kw[GROUPS_PER_WAVE][PP];
-#pragma unroll
-  for (int gi = 0; gi < GROUPS_PER_WAVE; ++gi) {
-    const int r = wave * 64 + gi * 16 + (lane & 15);
-    const bool ok = r < len;
-    const int64_t row = n0 + (ok ? r : 0);
-    const uint4* rp = (const uint4*)(kbase + esz * ((int64_t)b * p.batch_stride + row * p.seq_stride + (int64_t)kv * D));
-#pragma unroll
-    for (int pp = 0; pp < PP; ++pp) {
-      kw[gi][pp] = ok ? rp[4 * pp + slot] : make_uint4(0, 0, 0, 0);
-    }
-  }
+  const int64_t seq_bytes = (int64_t)Gm::ESZ * p.seq_stride;
+  const char* kbase = (const char*)p.K + (int64_t)Gm::ESZ * ((int64_t)b * p.batch_stride + (int64_t)kv * D);
+  auto chunk_len = [&](int tt) { return (int)min((int64_t)CHUNK, p.nk - (int64_t)tt * CHUNK); };
 
-  // ---- effective query of each head of the group, fp64 in LDS
+  // ---- first chunk's loads before anything else
+  uint4 r[Gm::NLD];
+  load_rows<D, BF16>(r, kbase, seq_bytes, (int64_t)t * CHUNK, chunk_len(t), tid);
+
+  // ---- effective query of each head of the group, fp64, staged in LDS then kept in registers
+  using P = Piece<BF16>;
   const char* qbase = (const char*)p.q;
   for (int i = tid; i < HMAX * D; i += THREADS) {
     const int g = i / D, e = i % D;
@@ -100,17 +183,17 @@ __global__ __launch_bounds__(THREADS) void score_kernel(Problem p) {
       const int g = i / D, e = i % D;
       const double v = qe[g][e];
       const double nrm = hnorm[g];
-      double r = 0.0;
+      double rr = 0.0;
       if (g < G && nrm > 0.0) {
         const double u = uniform53(p.seed, (uint32_t)e, (uint32_t)(h0 + g), (uint32_t)b, TAG_BERNOULLI);
-        if (u < fabs(v) / nrm) r = v > 0.0 ? 1.0 : (v < 0.0 ? -1.0 : 0.0);
+        if (u < fabs(v) / nrm) rr = v > 0.0 ? 1.0 : (v < 0.0 ? -1.0 : 0.0);
       }
-      qe[g][e] = r;
+      qe[g][e] = rr;
     }
     __syncthreads();
   }
-
-  // ---- B operand registers: head (quad*4 + (lane & 3)), dims EPL*(4*pp + slot) + e
+  // B operand of lane l: head (quad*4 + (l & 3)), dim EPL*(4*pp + slot) + e
+  const int slot = lane >> 4;
   double qb[NQ][PP][EPL];
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd)
@@ -118,98 +201,135 @@ __global__ __launch_bounds__(THREADS) void score_kernel(Problem p) {
     for (int pp = 0; pp < PP; ++pp)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) qb[qd][pp][e] = qe[qd * 4 + (lane & 3)][EPL * (4 * pp + slot) + e];
+  double mul[NQ];  // score multipliers of the heads this wave finalises (wave, wave + 4)
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) mul[j] = p.ternary ? hnorm[wave + 4 * j] : 1.0;
+  __syncthreads();  // the staging area is reused for scores
 
-  // ---- fp64 MFMA chains, one per 16-key group
+  for (; t < T; t += step) {
+    const int len = chunk_len(t);
+    const int64_t n0 = (int64_t)t * CHUNK;
+    store_rows<D, BF16>(ks, r, tid);
+    __syncthreads();
+    const int tn = t + step;
+    if (tn < T) load_rows<D, BF16>(r, kbase, seq_bytes, (int64_t)tn * CHUNK, chunk_len(tn), tid);
+
+    // ---- fp64 MFMA chains: one per 16-key group and head quad, interleaved
+    double acc[GROUPS_PER_WAVE][NQ];
 #pragma unroll
-  for (int gi = 0; gi < GROUPS_PER_WAVE; ++gi) {
-    double acc[NQ];
+    for (int gi = 0; gi < GROUPS_PER_WAVE; ++gi)
 #pragma unroll
-    for (int qd = 0; qd < NQ; ++qd) acc[qd] = 0.0;
+      for (int qd = 0; qd < NQ; ++qd) acc[gi][qd] = 0.0;
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp) {
-      double a[EPL];
-      P::to_f64(kw[gi][pp], a);
+      uint4 a4[GROUPS_PER_WAVE];
+#pragma unroll
+      for (int gi = 0; gi < GROUPS_PER_WAVE; ++gi)
+        a4[gi] = *(const uint4*)(ks + (wave * 64 + gi * 16 + (lane & 15)) * Gm::RSTRIDE + (4 * pp + slot) * 16);
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
 #pragma unroll
-        for (int qd = 0; qd < NQ; ++qd) acc[qd] = __builtin_amdgcn_mfma_f64_4x4x4f64(a[e], qb[qd][pp][e], acc[qd], 0, 0, 0);
-    }
-    const int key = wave * 64 + gi * 16 + 4 * ((lane >> 2) & 3) + (lane >> 4);
+        for (int gi = 0; gi < GROUPS_PER_WAVE; ++gi) {
+          const double a = piece_elem<BF16>(a4[gi], e);
 #pragma unroll
-    for (int qd = 0; qd < NQ; ++qd) sc[qd * 4 + (lane & 3)][key] = acc[qd];
-  }
-  __syncthreads();
+          for (int qd = 0; qd < NQ; ++qd)
+            acc[gi][qd] = __builtin_amdgcn_mfma_f64_4x4x4f64(a, qb[qd][pp][e], acc[gi][qd], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int gi = 0; gi < GROUPS_PER_WAVE; ++gi) {
+      const int key = wave * 64 + gi * 16 + 4 * ((lane >> 2) & 3) + (lane >> 4);
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) sc[qd * 4 + (lane & 3)][key] = acc[gi][qd];
+    }
+    __syncthreads();
 
-  // ---- per-head chunk max, exponentials and in-chunk prefix (thread = key)
-  const bool valid = tid < len;
-  double s[HMAX];
+    // ---- per-head chunk max, exponentials, in-chunk prefix: wave owns heads wave, wave + 4;
+    //      lane owns keys 4*lane .. 4*lane + 3
 #pragma unroll
-  for (int g = 0; g < HMAX; ++g) {
-    double v = sc[g][tid];
-    if (p.ternary) v = v * hnorm[g];
-    v = v * p.scale;
-    s[g] = valid ? v : -INFINITY;
-  }
+    for (int j = 0; j < NQ; ++j) {
+      const int g = wave + 4 * j;
+      if (g >= G) break;
+      double s[4];
+      double lmax = -INFINITY;
 #pragma unroll
-  for (int g = 0; g < HMAX; ++g) {
-    const double m = wave_max(s[g]);
-    if (lane == 0) red[wave][g] = m;
-  }
-  __syncthreads();
-  double cm[HMAX];
+      for (int i = 0; i < 4; ++i) {
+        const int k = 4 * lane + i;
+        double v = sc[g][k];
+        if (p.ternary) v = v * mul[j];
+        v = v * p.scale;
+        s[i] = k < len ? v : -INFINITY;
+        lmax = fmax(lmax, s[i]);
+      }
+      const double m = readlane_f64(wave_incl_max_dpp(lmax), 63);
+      double ex[4], pre[4], run = 0.0;
 #pragma unroll
-  for (int g = 0; g < HMAX; ++g) {
-    double m = red[0][g];
+      for (int i = 0; i < 4; ++i) {
+        ex[i] = (4 * lane + i) < len ? exp(s[i] - m) : 0.0;
+        run += ex[i];
+        pre[i] = run;
+      }
+      const double incl = wave_incl_scan_dpp(run);
+      double excl = __shfl_up(incl, 1, 64);
+      if (lane == 0) excl = 0.0;
+      const int64_t bh = (int64_t)b * p.H + h0 + g;
+      double* dst = p.stash + bh * p.nk + n0;
 #pragma unroll
-    for (int w = 1; w < THREADS / 64; ++w) m = fmax(m, red[w][g]);
-    cm[g] = m;
-  }
-  __syncthreads();
-  double ex[HMAX], pre[HMAX];
+      for (int i = 0; i < 4; ++i)
+        if (4 * lane + i < len) dst[4 * lane + i] = excl + pre[i];
+      if (p.prob) {
+        double* pr = p.prob + bh * p.nk + n0;
 #pragma unroll
-  for (int g = 0; g < HMAX; ++g) {
-    ex[g] = valid ? exp(s[g] - cm[g]) : 0.0;
-    pre[g] = wave_incl_scan(ex[g], lane);
-    if (lane == 63) red[wave][g] = pre[g];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < HMAX; ++g) {
-    double off = 0.0;
-    for (int w = 0; w < wave; ++w) off += red[w][g];
-    pre[g] += off;
-  }
-  const int64_t T = p.T;
-#pragma unroll
-  for (int g = 0; g < HMAX; ++g) {
-    if (g >= G) break;
-    const int64_t bh = (int64_t)b * p.H + h0 + g;
-    if (valid) {
-      p.stash[bh * p.nk + n0 + tid] = pre[g];
-      if (p.prob) p.prob[bh * p.nk + n0 + tid] = ex[g];
+        for (int i = 0; i < 4; ++i)
+          if (4 * lane + i < len) pr[4 * lane + i] = ex[i];
+      }
+      if (lane == 63) {
+        p.cmax[bh * T + t] = m;
+        p.csum[bh * T + t] = incl;
+      }
     }
-    if (tid == len - 1) {
-      p.cmax[bh * T + t] = cm[g];
-      p.csum[bh * T + t] = pre[g];
-    }
+    __syncthreads();  // ks and sc are rewritten by the next chunk
   }
+}
+
+template <int D, bool BF16, int NQ>
+constexpr int blocks_per_cu() {
+  constexpr size_t lds = (size_t)Geo<D, BF16>::LDS_K + 4 * NQ * CHUNK * sizeof(double) + 4 * NQ * sizeof(double);
+  return lds * 2 <= 160 * 1024 ? 2 : 1;
+}
+
+template <int D, bool BF16, int NQ>
+hipError_t launch_q(const Problem& p, hipStream_t st) {
+  constexpr int MINB = blocks_per_cu<D, BF16, NQ>();
+  score_kernel<D, BF16, NQ, MINB><<<dim3(p.score_blocks_per_group, p.Hkv, p.B), THREADS, 0, st>>>(p);
+  return hipGetLastError();
 }
 
 template <int D, bool BF16>
 hipError_t launch_d(const Problem& p, hipStream_t st) {
-  dim3 grid(p.T, p.Hkv, p.B);
-  if (p.G <= 4)
-    score_kernel<D, BF16, 1><<<grid, THREADS, 0, st>>>(p);
-  else
-    score_kernel<D, BF16, 2><<<grid, THREADS, 0, st>>>(p);
-  return hipGetLastError();
+  return p.G <= 4 ? launch_q<D, BF16, 1>(p, st) : launch_q<D, BF16, 2>(p, st);
 }
 
 }  // namespace
 
+int score_blocks_per_cu(int d, bool bf16, int G) {
+  const bool q1 = G <= 4;
+  if (d == 128) {
+    if (bf16) return q1 ? blocks_per_cu<128, true, 1>() : blocks_per_cu<128, true, 2>();
+    return q1 ? blocks_per_cu<128, false, 1>() : blocks_per_cu<128, false, 2>();
+  }
+  if (bf16) return q1 ? blocks_per_cu<64, true, 1>() : blocks_per_cu<64, true, 2>();
+  return q1 ? blocks_per_cu<64, false, 1>() : blocks_per_cu<64, false, 2>();
+}
+
 hipError_t launch_score(const Problem& p, hipStream_t st) {
   if (p.d == 128) return p.bf16 ? launch_d<128, true>(p, st) : launch_d<128, false>(p, st);
   return p.bf16 ? launch_d<64, true>(p, st) : launch_d<64, false>(p, st);
+}
+
+hipError_t launch_chunk_cdf(const Problem& p, hipStream_t st) {
+  chunk_cdf_kernel<<<dim3(p.Hkv, p.B), THREADS, 0, st>>>(p);
+  return hipGetLastError();
 }
 
 }  // namespace santa

@@ -70,7 +70,6 @@ def _args(**kw):
     (dict(heads=32, kv_heads=2), santa.ERR_UNSUPPORTED),
     (dict(nk=(1 << 20) + 1), santa.ERR_UNSUPPORTED),
     (dict(S=70000), santa.ERR_UNSUPPORTED),
-    (dict(heads=16, kv_heads=2, S=4096), santa.ERR_UNSUPPORTED),
     (dict(kv_seq_stride=100), santa.ERR_INVALID_ARG),
     (dict(kv_seq_stride=257), santa.ERR_INVALID_ARG),
     (dict(K=0x2008), santa.ERR_INVALID_ARG),
@@ -100,7 +99,9 @@ def test_workspace_bytes(L):
     B, nk, H, Hkv, S = 2, 1000, 8, 2, 16
     T = (nk + 255) // 256
     n = santa.workspace_bytes(B, nk, H, Hkv, 128, S)
-    assert n >= B * H * nk * 8 + 2 * B * H * T * 8 + B * H * S * 4 + B * Hkv * 4
+    G = H // Hkv
+    assert n >= (B * Hkv * 4 + B * H * nk * 8 + 3 * B * H * T * 8 + B * H * (T + 1) * 8 + B * H * 4
+                 + B * Hkv * G * S * 32 + B * H * S * 4 + B * Hkv * 4)
     assert n % 256 == 0
     assert santa.workspace_bytes(1, 0, 8, 2, 128, S) == 0
     assert santa.workspace_bytes(1, 10, 6, 4, 128, S) == 0

@@ -202,7 +202,7 @@ def test_gpu_estimator_unbiased_4096_seeds():
     w = workloads.make(1)
     dev = torch.device("cuda:0")
     qd, Kd, Vd = w.q.to(dev), w.K.to(dev), w.V.to(dev)
-    ws = torch.empty(santa.workspace_bytes(1, w.nk, 1, 1, w.d, w.S), dtype=torch.uint8, device=dev)
+    ws = santa.new_workspace(santa.workspace_bytes(1, w.nk, 1, 1, w.d, w.S), dev)
     outs = torch.empty((4096, w.d), dtype=torch.float32, device=dev)
     for seed in range(4096):
         santa.decode(qd, Kd, Vd, w.S, "iid", seed, out=outs[seed].view(1, 1, w.d), workspace=ws)
