@@ -4,7 +4,7 @@ Workload (default): Llama-3.1-8B-shaped single-layer decode, batch 1, 32 query /
 bf16 K/V cache of nk=32768 positions with 32 planted aligned keys per query head, stratified sampling
 with S=256 (seeded synthetic inputs, resident in HBM before timing).
 
-A step is one call of santa_decode_ex (score -> chunk CDF -> resolve -> gather), timed with HIP events on the
+A step is one call of santa_decode_ex (score -> chunk CDF -> resolve+gather per chunk -> merge), timed with HIP events on the
 launching stream. Before every timed step a 1 GiB in-place update evicts K/V from the caches (the
 256 MB Infinity Cache would otherwise hold the 64 MiB K), outside the events, like the cold-cache
 protocol of the paper's kernel benchmark (Appendix Q). Reported alongside:
@@ -174,7 +174,7 @@ def main():
         "us_min": round(min(us), 3),
         "us_warm_median": round(statistics.median(us_warm), 3),
         "stage_us_mean": {"score": round(score_us, 3), "cdf_resolve": round(float(np.mean(stage[:, 1])), 3),
-                          "gather": round(float(np.mean(stage[:, 2])), 3),
+                          "merge": round(float(np.mean(stage[:, 2])), 3),
                           "total_with_events": round(float(np.mean(stage[:, 3])), 3)},
         "roofline": {
             "kernel": "score (split-K fp64 MFMA scores + chunk max/sum-exp + in-chunk prefix)",

@@ -11,7 +11,8 @@
  *      Eq. 4), stratified or systematic (S²ANTA, Section 2.1), with the half-open convention
  *      1{F(j-1) <= t < F(j)} of Appendix A.4;
  *   4. a gather-and-add of the sampled V rows, each row read once per GQA group and weighted by its
- *      sample count (Appendix O, Algorithm 5), scaled by 1/S (Section 2, Eq. 4).
+ *      sample count, per (KV head, chunk) with an fp32 accumulator (Appendix O, Algorithm 5), then the
+ *      chunk sums added per head and scaled by 1/S (Section 2, Eq. 4).
  *
  * Conventions shared by every entry point:
  *   - Device pointers are caller-owned; the library never frees or retains them past the call.
@@ -87,21 +88,21 @@ typedef struct santa_args {
   int32_t reserved0;
   uint64_t seed;
   void* stream;              /* hipStream_t, NULL = default stream */
-  void* workspace;           /* device scratch of at least santa_workspace_bytes() bytes; zero-filled before
-                                its first use (its leading counters must start at zero; every completed
-                                call leaves them zero, so it can be reused by later, non-overlapping calls) */
+  void* workspace;           /* device scratch of at least santa_workspace_bytes() bytes; no initial contents
+                                are required (every call writes each part before reading it); calls that
+                                share it must not overlap */
   size_t workspace_bytes;
   /* optional debug outputs; NULL to skip */
   int32_t* idx_out;          /* device [batch, heads, S]: sampled key index of each point, in point order */
   double* prob_out;          /* device [batch, heads, nk]: softmax probabilities */
   santa_stats* stats_out;    /* host; the call synchronises the stream to fill it */
-  float* stage_ms;           /* host float[4]: GPU time of [score, chunk CDF + resolve, gather, whole call]
+  float* stage_ms;           /* host float[4]: GPU time of [score, chunk CDF + resolve, merge, whole call]
                                 from events between the launches; synchronises the stream */
 } santa_args;
 
 /*
  * santa_decode — one SANTA / S²ANTA decode step in its simplest form: batch 1, bf16 q/K/V/out,
- * contiguous [nk, kv_heads, d] caches, the default stream, and a zero-filled workspace the library
+ * contiguous [nk, kv_heads, d] caches, the default stream, and a workspace the library
  * allocates on first use and keeps (grow-only, per device) until santa_release(). Calls on one device
  * share that workspace and must not overlap. Returns a status code.
  */
@@ -109,15 +110,15 @@ int santa_decode(const void* q, const void* K, const void* V, int64_t nk, int he
                  int mode, uint64_t seed, void* out);
 
 /*
- * santa_decode_ex — the full form. Caller-owned workspace (`workspace`, `workspace_bytes`, zero-filled
- * before first use); never allocates device memory. Launches four kernels on `stream`: the split-K score
- * pass, the chunk CDF per KV group, the sampling pass per chunk (which lists each group's distinct
- * sampled rows with per-head counts) and the gather per KV group. Calls sharing one workspace must not
- * overlap.
+ * santa_decode_ex — the full form. Caller-owned workspace (`workspace`, `workspace_bytes`); never
+ * allocates device memory. Launches four kernels on `stream`: the split-K score pass, the chunk CDF per
+ * KV group, the sampling and gather-add per (chunk, KV group) (each distinct sampled row read once and
+ * added with its per-head counts into an fp32 chunk partial), and the merge that adds the chunk partials
+ * of each head and scales by 1/S. Calls sharing one workspace must not overlap.
  */
 int santa_decode_ex(const santa_args* a);
 
-/* Workspace bytes santa_decode_ex needs for these sizes (0 if the sizes are invalid). */
+/* Workspace bytes santa_decode_ex needs for these sizes (0 if the sizes are invalid or d is unsupported). */
 size_t santa_workspace_bytes(int batch, int64_t nk, int heads, int kv_heads, int d, int S, int mode);
 
 /*

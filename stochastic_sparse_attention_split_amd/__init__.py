@@ -131,9 +131,9 @@ def workspace_bytes(B: int, nk: int, H: int, Hkv: int, d: int, S: int, mode=STRA
 
 
 def new_workspace(nbytes: int, device) -> torch.Tensor:
-    """A zero-filled workspace for decode(): the library's counters must start at zero; every completed
-    call leaves them at zero again, so a workspace can be reused across calls (not concurrently)."""
-    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    """A workspace for decode(). No initial contents are required; it can be reused by later calls that do
+    not overlap with each other."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 def dense_workspace_bytes(B: int, nk: int, H: int, Hkv: int, d: int) -> int:
@@ -170,8 +170,7 @@ def decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="stra
     """One SANTA / S²ANTA decode step through santa_decode_ex.
 
     Returns out, or (out, info) when stats or stage_ms is requested (info holds the stats fields and the
-    per-kernel milliseconds [score, chunk CDF + resolve, gather, total]). A caller-provided workspace must have been
-    zero-filled before its first use (see new_workspace).
+    milliseconds [score, chunk CDF + resolve, merge, total] from events between the launches).
     """
     if out is None:
         out = torch.empty_like(q)

@@ -105,6 +105,16 @@ struct Piece<true> {
     o[6] = (double)bf16_lo(w.w);
     o[7] = (double)bf16_hi(w.w);
   }
+  __device__ static inline void to_f32(const uint4& w, float* o) {
+    o[0] = bf16_lo(w.x);
+    o[1] = bf16_hi(w.x);
+    o[2] = bf16_lo(w.y);
+    o[3] = bf16_hi(w.y);
+    o[4] = bf16_lo(w.z);
+    o[5] = bf16_hi(w.z);
+    o[6] = bf16_lo(w.w);
+    o[7] = bf16_hi(w.w);
+  }
   __device__ static inline double elem(const void* base, int64_t i) {
     return (double)__uint_as_float(((uint32_t)((const uint16_t*)base)[i]) << 16);
   }
@@ -118,6 +128,12 @@ struct Piece<false> {
     o[1] = (double)__uint_as_float(w.y);
     o[2] = (double)__uint_as_float(w.z);
     o[3] = (double)__uint_as_float(w.w);
+  }
+  __device__ static inline void to_f32(const uint4& w, float* o) {
+    o[0] = __uint_as_float(w.x);
+    o[1] = __uint_as_float(w.y);
+    o[2] = __uint_as_float(w.z);
+    o[3] = __uint_as_float(w.w);
   }
   __device__ static inline double elem(const void* base, int64_t i) { return (double)((const float*)base)[i]; }
 };
@@ -167,14 +183,6 @@ __device__ inline double readlane_f64(double v, int l) {
 // ---------------------------------------------------------------------------------------------
 // problem description passed to kernels
 
-// one distinct sampled V row of a (KV head, sequence) group: key index and 16-bit per-head counts
-struct RowRecord {
-  int32_t key;
-  uint32_t counts[4];  // head g in the low (g even) or high (g odd) half of counts[g / 2]
-  int32_t pad[3];
-};
-static_assert(sizeof(RowRecord) == 32, "two 16-byte loads per record");
-
 struct Problem {
   const void* q;
   const void* K;
@@ -192,17 +200,16 @@ struct Problem {
   double scale;          // 1/sqrt(d), formed on the host in fp64
   int T;                 // chunks per sequence
   int score_blocks_per_group;  // score blocks per (KV head, sequence); each loops over chunks
-  // workspace
-  int32_t* counters;     // [B*Hkv] row-list lengths; zero between calls
+  // workspace (no initial contents required: every call writes what it later reads)
   double* stash;         // [B, H, nk] in-chunk inclusive prefix of exp(s - m_t)
   double* cmax;          // [B, H, T] chunk max m_t
   double* csum;          // [B, H, T] chunk sum-exp l_t
   double* cdf;           // [B, H, T+1] exclusive prefix of W_t = l_t exp(m_t - m*); cdf[T] = Z
   double* cscale;        // [B, H, T] exp(m_t - m*)
   int32_t* lastpos;      // [B, H] last chunk with W_t > 0
-  RowRecord* rows;       // [B*Hkv][G*S] distinct sampled rows per group
+  float* partial;        // [B, Hkv, T, G, d] per-chunk sums of count * V (fp32, exact products)
   int32_t* idx;          // [B, H, S]
-  int32_t* unique;       // [B, Hkv]
+  int32_t* unique;       // [B, Hkv, T] distinct sampled keys of each chunk
   double* prob;          // optional [B, H, nk]
 };
 

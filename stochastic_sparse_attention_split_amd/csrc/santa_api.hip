@@ -1,5 +1,5 @@
 // C ABI of libsanta.so: argument validation (before any HIP call), workspace layout, and the launch
-// sequence score -> chunk CDF -> resolve -> gather on the caller's stream. See include/santa.h.
+// sequence score -> chunk CDF -> resolve (sample + gather per chunk) -> merge on the caller's stream.
 
 #include <cmath>
 #include <cstdarg>
@@ -37,11 +37,11 @@ constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-  size_t counters, stash, cmax, csum, cdf, cscale, lastpos, rows, idx, unique, total;
+  size_t stash, cmax, csum, cdf, cscale, lastpos, partial, idx, unique, total;
 };
 
-// counters first: the only part of the workspace that must be zero before its first use
-Layout layout(int64_t B, int64_t nk, int64_t H, int64_t Hkv, int64_t S) {
+// every region is written by the call before it is read: no initial contents are required
+Layout layout(int64_t B, int64_t nk, int64_t H, int64_t Hkv, int64_t d, int64_t S) {
   const int64_t T = (nk + CHUNK - 1) / CHUNK;
   const int64_t G = H / Hkv;
   Layout L;
@@ -51,16 +51,15 @@ Layout layout(int64_t B, int64_t nk, int64_t H, int64_t Hkv, int64_t S) {
     off = align_up(off + bytes);
     return at;
   };
-  L.counters = take((size_t)(B * Hkv) * sizeof(int32_t));
   L.stash = take((size_t)(B * H * nk) * sizeof(double));
   L.cmax = take((size_t)(B * H * T) * sizeof(double));
   L.csum = take((size_t)(B * H * T) * sizeof(double));
   L.cdf = take((size_t)(B * H * (T + 1)) * sizeof(double));
   L.cscale = take((size_t)(B * H * T) * sizeof(double));
   L.lastpos = take((size_t)(B * H) * sizeof(int32_t));
-  L.rows = take((size_t)(B * Hkv * G * S) * sizeof(RowRecord));
+  L.partial = take((size_t)(B * Hkv * T * G * d) * sizeof(float));
   L.idx = take((size_t)(B * H * S) * sizeof(int32_t));
-  L.unique = take((size_t)(B * Hkv) * sizeof(int32_t));
+  L.unique = take((size_t)(B * Hkv * T) * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -144,10 +143,10 @@ struct Events {
 extern "C" {
 
 size_t santa_workspace_bytes(int batch, int64_t nk, int heads, int kv_heads, int d, int S, int mode) {
-  (void)d;
   (void)mode;
   if (batch < 1 || nk < 1 || heads < 1 || kv_heads < 1 || S < 1 || heads % kv_heads) return 0;
-  return layout(batch, nk, heads, kv_heads, S).total;
+  if (d != 64 && d != 128) return 0;
+  return layout(batch, nk, heads, kv_heads, d, S).total;
 }
 
 int santa_decode_ex(const santa_args* a) {
@@ -155,7 +154,7 @@ int santa_decode_ex(const santa_args* a) {
   int64_t seq = 0, bstride = 0;
   int st = validate_sampled(a, &seq, &bstride);
   if (st) return st;
-  const Layout L = layout(a->batch, a->nk, a->heads, a->kv_heads, a->S);
+  const Layout L = layout(a->batch, a->nk, a->heads, a->kv_heads, a->d, a->S);
   if (!a->workspace || a->workspace_bytes < L.total)
     return fail(SANTA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", a->workspace_bytes,
                 L.total);
@@ -182,14 +181,13 @@ int santa_decode_ex(const santa_args* a) {
   p.scale = 1.0 / std::sqrt((double)a->d);
   p.T = (int)((a->nk + CHUNK - 1) / CHUNK);
   p.score_blocks_per_group = score_blocks_per_group(p.B * p.Hkv, p.T, score_blocks_per_cu(p.d, p.bf16, p.G));
-  p.counters = (int32_t*)(ws + L.counters);
   p.stash = (double*)(ws + L.stash);
   p.cmax = (double*)(ws + L.cmax);
   p.csum = (double*)(ws + L.csum);
   p.cdf = (double*)(ws + L.cdf);
   p.cscale = (double*)(ws + L.cscale);
   p.lastpos = (int32_t*)(ws + L.lastpos);
-  p.rows = (RowRecord*)(ws + L.rows);
+  p.partial = (float*)(ws + L.partial);
   p.idx = a->idx_out ? a->idx_out : (int32_t*)(ws + L.idx);
   p.unique = (int32_t*)(ws + L.unique);
   p.prob = a->prob_out;
@@ -211,11 +209,11 @@ int santa_decode_ex(const santa_args* a) {
   if ((e = launch_chunk_cdf(p, stream)) != hipSuccess) return hip_fail(e, "chunk CDF kernel launch");
   if ((e = launch_resolve(p, stream)) != hipSuccess) return hip_fail(e, "resolve kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  if ((e = launch_gather(p, stream)) != hipSuccess) return hip_fail(e, "gather kernel launch");
+  if ((e = launch_merge(p, stream)) != hipSuccess) return hip_fail(e, "merge kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
   if (a->stats_out) {
-    std::vector<int32_t> u((size_t)a->batch * a->kv_heads);
+    std::vector<int32_t> u((size_t)a->batch * a->kv_heads * p.T);
     if ((e = hipMemcpyAsync(u.data(), p.unique, u.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream)) !=
         hipSuccess)
       return hip_fail(e, "hipMemcpyAsync(unique)");
@@ -276,7 +274,7 @@ int santa_decode(const void* q, const void* K, const void* V, int64_t nk, int he
   int64_t seq, bs;
   int st = validate_sampled(&a, &seq, &bs);
   if (st) return st;
-  const size_t need = layout(1, nk, heads, kv_heads, S).total;
+  const size_t need = layout(1, nk, heads, kv_heads, d, S).total;
   std::lock_guard<std::mutex> lock(g_ws_mu);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -291,7 +289,6 @@ int santa_decode(const void* q, const void* K, const void* V, int64_t nk, int he
       w.bytes = 0;
     }
     if ((e = hipMalloc(&w.ptr, need)) != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
-    if ((e = hipMemset(w.ptr, 0, need)) != hipSuccess) return hip_fail(e, "hipMemset(workspace)");
     w.bytes = need;
   }
   a.workspace = w.ptr;

@@ -60,13 +60,14 @@ struct Geo {
 };
 
 // full-row loads of chunk rows [n0, n0+len): load i covers row i*RPI + tid/NPR, piece tid%NPR; rows past
-// the end re-read row n0 (always valid) so every load is unconditional; those keys are masked later
-template <int D, bool BF16>
+// the end re-read row n0 (always valid) so every load is unconditional; those keys are masked later.
+// Loads [I0, I0 + N) only, so that a prefetch can be spread over the MFMA loop.
+template <int D, bool BF16, int I0 = 0, int N = Geo<D, BF16>::NLD>
 __device__ inline void load_rows(uint4* r, const char* kbase, int64_t seq_bytes, int64_t n0, int len, int tid) {
   using Gm = Geo<D, BF16>;
   const int piece = tid % Gm::NPR, row0 = tid / Gm::NPR;
 #pragma unroll
-  for (int i = 0; i < Gm::NLD; ++i) {
+  for (int i = I0; i < I0 + N; ++i) {
     const int row = i * Gm::RPI + row0;
     r[i] = load_stream16(kbase + (n0 + (row < len ? row : 0)) * seq_bytes + piece * 16);
   }
@@ -84,6 +85,76 @@ __device__ inline void store_rows(unsigned char* ks, const uint4* r, int tid) {
 // heads of one (KV head, sequence) group, one wave per head (waves take heads wave, wave + 4): lane l owns
 // a contiguous run of chunks; the prefix is exclusive, then made monotone by a running maximum so that
 // the chunks' intervals [cdf_t, cdf_{t+1}) partition [0, Z) exactly. cdf[T] = Z. One block per group.
+// Register form: T <= 64 * PER and lane l owns chunks [l*PER, l*PER + PER), held in registers, so the statistics
+// are read in one round trip. The plain form below takes any T: lane l owns a contiguous run of ceil(T/64)
+// chunks, re-read from memory between the steps.
+template <int PER>
+__global__ __launch_bounds__(THREADS) void chunk_cdf_reg_kernel(Problem p) {
+  const int kv = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h0 = kv * p.G;
+  const int T = p.T;
+  const int t0 = lane * PER;
+  for (int g = wave; g < p.G; g += THREADS / 64) {
+    const int64_t bh = (int64_t)b * p.H + h0 + g;
+    const double* cm = p.cmax + bh * T;
+    const double* cs = p.csum + bh * T;
+    double m[PER], l[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int tt = min(t0 + j, T - 1);  // every lane loads a valid address; extra entries are masked
+      m[j] = cm[tt];
+      l[j] = cs[tt];
+    }
+    double mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (t0 + j < T) mx = fmax(mx, m[j]);
+    const double ms = readlane_f64(wave_incl_max_dpp(mx), 63);
+    double f[PER], loc[PER], run = 0.0;
+    int lp = -1;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const bool valid = t0 + j < T;
+      f[j] = valid ? exp(m[j] - ms) : 0.0;
+      const double w = l[j] * f[j];
+      loc[j] = run;  // local exclusive prefix, offset below
+      run += w;
+      if (valid && w > 0.0) lp = t0 + j;
+    }
+    const double incl = wave_incl_scan_dpp(run);
+    double excl = __shfl_up(incl, 1, 64);
+    if (lane == 0) excl = 0.0;
+    double lmax = 0.0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const double c = fmax(excl + loc[j], lmax);
+      loc[j] = c;
+      lmax = c;
+    }
+    // running maximum across lanes: lane l's values are raised to the maximum of all earlier lanes
+    const double pmax = wave_incl_max_dpp(t0 < T ? lmax : 0.0);
+    double before = __shfl_up(pmax, 1, 64);
+    if (lane == 0) before = 0.0;
+    double* cdf = p.cdf + bh * (T + 1);
+    double* csc = p.cscale + bh * T;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (t0 + j < T) {
+        cdf[t0 + j] = fmax(loc[j], before);
+        csc[t0 + j] = f[j];
+      }
+    }
+    const double Z = readlane_f64(incl, 63);
+    const double top = readlane_f64(pmax, 63);
+    const double lpd = readlane_f64(wave_incl_max_dpp((double)lp), 63);
+    if (lane == 0) {
+      cdf[T] = fmax(Z, top);
+      p.lastpos[bh] = (int32_t)lpd;
+    }
+  }
+}
+
 __global__ __launch_bounds__(THREADS) void chunk_cdf_kernel(Problem p) {
   const int kv = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -206,22 +277,60 @@ __global__ __launch_bounds__(THREADS, MINB) void score_kernel(Problem p) {
   for (int j = 0; j < NQ; ++j) mul[j] = p.ternary ? hnorm[wave + 4 * j] : 1.0;
   __syncthreads();  // the staging area is reused for scores
 
+  // Results of a chunk (stash prefixes, chunk max and sum) are held in registers and stored after the
+  // next chunk's K tile has reached LDS and before its prefetch is issued: stores issued behind a full
+  // queue of streaming loads would stall the wave until those loads drain.
+  double pend[NQ][4];
+  double pend_m[NQ], pend_l[NQ];
+  int64_t pend_n0 = -1;
+  int pend_len = 0, pend_t = 0;
+  auto flush = [&]() {
+    if (pend_n0 < 0) return;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int g = wave + 4 * j;
+      if (g >= G) break;
+      const int64_t bh = (int64_t)b * p.H + h0 + g;
+      double* dst = p.stash + bh * p.nk + pend_n0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * lane + i < pend_len) dst[4 * lane + i] = pend[j][i];
+      if (lane == 63) {
+        p.cmax[bh * T + pend_t] = pend_m[j];
+        p.csum[bh * T + pend_t] = pend_l[j];
+      }
+    }
+  };
+
   for (; t < T; t += step) {
     const int len = chunk_len(t);
     const int64_t n0 = (int64_t)t * CHUNK;
     store_rows<D, BF16>(ks, r, tid);
     __syncthreads();
+    flush();
     const int tn = t + step;
-    if (tn < T) load_rows<D, BF16>(r, kbase, seq_bytes, (int64_t)tn * CHUNK, chunk_len(tn), tid);
+    const bool more = tn < T;
+    const int64_t nn0 = (int64_t)tn * CHUNK;
+    const int nlen = more ? chunk_len(tn) : 0;
 
-    // ---- fp64 MFMA chains: one per 16-key group and head quad, interleaved
+    // ---- fp64 MFMA chains: one per 16-key group and head quad, interleaved; the next chunk's loads
+    //      are spread over the pieces
     double acc[GROUPS_PER_WAVE][NQ];
 #pragma unroll
     for (int gi = 0; gi < GROUPS_PER_WAVE; ++gi)
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) acc[gi][qd] = 0.0;
+    static_assert(Gm::NLD % PP == 0, "prefetch split over the pieces");
+    constexpr int LPP = Gm::NLD / PP;
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp) {
+      if (more) {
+        switch (pp) {  // compile-time ranges; pp is unrolled
+#define SANTA_PF(k) case k: if constexpr (k < PP) load_rows<D, BF16, k * LPP, LPP>(r, kbase, seq_bytes, nn0, nlen, tid); break;
+          SANTA_PF(0) SANTA_PF(1) SANTA_PF(2) SANTA_PF(3) SANTA_PF(4) SANTA_PF(5) SANTA_PF(6) SANTA_PF(7)
+#undef SANTA_PF
+        }
+      }
       uint4 a4[GROUPS_PER_WAVE];
 #pragma unroll
       for (int gi = 0; gi < GROUPS_PER_WAVE; ++gi)
@@ -272,24 +381,23 @@ __global__ __launch_bounds__(THREADS, MINB) void score_kernel(Problem p) {
       const double incl = wave_incl_scan_dpp(run);
       double excl = __shfl_up(incl, 1, 64);
       if (lane == 0) excl = 0.0;
-      const int64_t bh = (int64_t)b * p.H + h0 + g;
-      double* dst = p.stash + bh * p.nk + n0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * lane + i < len) dst[4 * lane + i] = excl + pre[i];
+      for (int i = 0; i < 4; ++i) pend[j][i] = excl + pre[i];
+      pend_m[j] = m;
+      pend_l[j] = incl;
       if (p.prob) {
-        double* pr = p.prob + bh * p.nk + n0;
+        double* pr = p.prob + ((int64_t)b * p.H + h0 + g) * p.nk + n0;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (4 * lane + i < len) pr[4 * lane + i] = ex[i];
       }
-      if (lane == 63) {
-        p.cmax[bh * T + t] = m;
-        p.csum[bh * T + t] = incl;
-      }
     }
+    pend_n0 = n0;
+    pend_len = len;
+    pend_t = t;
     __syncthreads();  // ks and sc are rewritten by the next chunk
   }
+  flush();
 }
 
 template <int D, bool BF16, int NQ>
@@ -328,7 +436,19 @@ hipError_t launch_score(const Problem& p, hipStream_t st) {
 }
 
 hipError_t launch_chunk_cdf(const Problem& p, hipStream_t st) {
-  chunk_cdf_kernel<<<dim3(p.Hkv, p.B), THREADS, 0, st>>>(p);
+  const dim3 grid(p.Hkv, p.B);
+  if (p.T <= 64)
+    chunk_cdf_reg_kernel<1><<<grid, THREADS, 0, st>>>(p);
+  else if (p.T <= 128)
+    chunk_cdf_reg_kernel<2><<<grid, THREADS, 0, st>>>(p);
+  else if (p.T <= 256)
+    chunk_cdf_reg_kernel<4><<<grid, THREADS, 0, st>>>(p);
+  else if (p.T <= 512)
+    chunk_cdf_reg_kernel<8><<<grid, THREADS, 0, st>>>(p);
+  else if (p.T <= 1024)
+    chunk_cdf_reg_kernel<16><<<grid, THREADS, 0, st>>>(p);
+  else
+    chunk_cdf_kernel<<<grid, THREADS, 0, st>>>(p);
   return hipGetLastError();
 }
 

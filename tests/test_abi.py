@@ -100,11 +100,12 @@ def test_workspace_bytes(L):
     T = (nk + 255) // 256
     n = santa.workspace_bytes(B, nk, H, Hkv, 128, S)
     G = H // Hkv
-    assert n >= (B * Hkv * 4 + B * H * nk * 8 + 3 * B * H * T * 8 + B * H * (T + 1) * 8 + B * H * 4
-                 + B * Hkv * G * S * 32 + B * H * S * 4 + B * Hkv * 4)
+    assert n >= (B * H * nk * 8 + 3 * B * H * T * 8 + B * H * (T + 1) * 8 + B * H * 4
+                 + B * Hkv * T * G * 128 * 4 + B * H * S * 4 + B * Hkv * T * 4)
     assert n % 256 == 0
     assert santa.workspace_bytes(1, 0, 8, 2, 128, S) == 0
     assert santa.workspace_bytes(1, 10, 6, 4, 128, S) == 0
+    assert santa.workspace_bytes(1, 10, 8, 2, 96, S) == 0
     assert santa.dense_workspace_bytes(1, 1024, 8, 2, 128) >= 8 * 2 * 130 * 4
     assert santa.dense_workspace_bytes(1, 1024, 8, 2, 96) == 0
 

@@ -49,6 +49,9 @@ SMALL = [
     (1, 4, 1, 64, 1500, "bf16", "sys", 1000, True, 2),
     (1, 8, 2, 128, 2000, "bf16", "strat", 1, False, 4),
     (1, 8, 2, 128, 2000, "bf16", "sys", 3, False, 4),
+    (1, 6, 2, 128, 1300, "bf16", "strat", 50, False, 3),   # G = 3 (group tile wider than the group)
+    (1, 5, 1, 64, 900, "bf16", "iid", 20, False, 2),       # G = 5
+    (1, 6, 1, 128, 1800, "f32", "sys", 40, False, 2),      # G = 6, fp32
 ]
 
 
@@ -84,6 +87,40 @@ def test_strided_caches():
     r = oracle.decode(q.float().numpy(), K[:, :nk].float().numpy(), V[:, :nk].float().numpy(), 64, oracle.STRAT, 5)
     assert np.array_equal(idx.cpu().numpy(), r.idx)
     assert np.max(np.abs(out.float().cpu().numpy() - r.out)) <= 2e-2
+
+
+@pytest.mark.parametrize("nk", [40000, 100000, 200000, 300000])
+def test_long_sequences_every_chunk_cdf_form(nk):
+    """T = 157, 391, 782 and 1172 chunks: the register forms of the chunk CDF for 4, 8 and 16 chunks per
+    lane, and the looped form beyond 1024 chunks."""
+    log(f"long sequence nk={nk}")
+    q, K, V, _ = workloads.make_inputs(1, 4, 1, 64, nk, dtype="bf16", spikes_per_head=6, rng_seed=nk & 0xFFFF)
+    rep, *_ = compare(q, K, V, 512, "strat", 11, dtype="bf16", want_prob=(nk <= 100000), label=f"nk={nk}")
+    log(f"  {rep}")
+
+
+def test_workspace_needs_no_initial_contents():
+    """A workspace full of garbage (NaN bit patterns) and one reused after a larger call give the same
+    result as a fresh one."""
+    log("workspace contents")
+    dev = torch.device("cuda:0")
+    q, K, V, _ = workloads.make_inputs(2, 8, 2, 128, 3000, dtype="bf16", spikes_per_head=4, rng_seed=41)
+    qd, Kd, Vd = q.to(dev), K.to(dev), V.to(dev)
+    n = santa.workspace_bytes(2, 3000, 8, 2, 128, 64)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=dev)
+    i1 = torch.empty((2, 8, 64), dtype=torch.int32, device=dev)
+    a = santa.decode(qd, Kd, Vd, 64, "strat", 8, workspace=ws, idx_out=i1)
+    torch.cuda.synchronize()
+    big = workloads.make_inputs(2, 8, 2, 128, 2900, dtype="bf16", spikes_per_head=2, rng_seed=42)
+    santa.decode(big[0].to(dev), big[1].to(dev), big[2].to(dev), 64, "iid", 3, workspace=ws)
+    i2 = torch.empty_like(i1)
+    b = santa.decode(qd, Kd, Vd, 64, "strat", 8, workspace=ws, idx_out=i2)
+    c = santa.decode(qd, Kd, Vd, 64, "strat", 8)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    assert torch.equal(a, b) and torch.equal(a, c)
+    r = oracle.decode(q.float().numpy(), K.float().numpy(), V.float().numpy(), 64, oracle.STRAT, 8)
+    assert np.array_equal(i1.cpu().numpy(), r.idx)
 
 
 def test_workload_2_full_size():
