@@ -12,6 +12,7 @@ namespace santa {
 constexpr int CHUNK = 256;
 constexpr int MAX_CHUNKS = 4096;          // nk <= 2^20 per sequence
 constexpr int MAX_GROUP = 8;              // query heads per KV head handled by one score block
+constexpr int FUSED_CDF_MAX_T = 128;  // up to this many chunks the sampling kernel builds the chunk CDF itself
 
 // ---------------------------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11):
@@ -181,6 +182,69 @@ __device__ inline double readlane_f64(double v, int l) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Chunk CDF of one head, computed by one wave ("Stochastic Sparse Attention for Memory-Bound Inference",
+// Appendix O, Algorithm 4: m* = max_t m_t, W_t = l_t exp(m_t - m*), Z = sum_t W_t). Lane l owns chunks
+// [l*PER, l*PER + PER) (T <= 64 * PER). The exclusive prefix is made monotone by a running maximum so
+// that the intervals [C_t, C_{t+1}) partition [0, C_T) exactly; C_T = max(Z, that maximum). The inputs
+// m[j], l[j] are the lane's chunk statistics (entries at t >= T are ignored).
+template <int PER>
+struct ChunkCdf {
+  double c[PER];  // C_t
+  double f[PER];  // exp(m_t - m*)
+  double top;     // C_T (wave-uniform)
+  int last;       // last chunk with W_t > 0 (wave-uniform)
+};
+
+template <int PER>
+__device__ inline void chunk_cdf_wave(const double* m, const double* l, int T, int lane, ChunkCdf<PER>& o) {
+  const int t0 = lane * PER;
+  double mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (t0 + j < T) mx = fmax(mx, m[j]);
+  const double ms = readlane_f64(wave_incl_max_dpp(mx), 63);
+  double loc[PER], run = 0.0;
+  int lp = -1;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const bool valid = t0 + j < T;
+    o.f[j] = valid ? exp(m[j] - ms) : 0.0;
+    const double w = l[j] * o.f[j];
+    loc[j] = run;  // local exclusive prefix, offset below
+    run += w;
+    if (valid && w > 0.0) lp = t0 + j;
+  }
+  const double incl = wave_incl_scan_dpp(run);
+  double excl = __shfl_up(incl, 1, 64);
+  if (lane == 0) excl = 0.0;
+  double lmax = 0.0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const double c = fmax(excl + loc[j], lmax);
+    loc[j] = c;
+    lmax = c;
+  }
+  // running maximum across lanes: lane l's values are raised to the maximum of all earlier lanes
+  const double pmax = wave_incl_max_dpp(t0 < T ? lmax : 0.0);
+  double before = __shfl_up(pmax, 1, 64);
+  if (lane == 0) before = 0.0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) o.c[j] = fmax(loc[j], before);
+  o.top = fmax(readlane_f64(incl, 63), readlane_f64(pmax, 63));
+  o.last = (int)readlane_f64(wave_incl_max_dpp((double)lp), 63);
+}
+
+// element j (wave-uniform) of a small register array
+template <int N>
+__device__ inline double pick(const double* a, int j) {
+  double v = a[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i)
+    if (j == i) v = a[i];
+  return v;
+}
+
+// ---------------------------------------------------------------------------------------------
 // problem description passed to kernels
 
 struct Problem {
@@ -201,7 +265,8 @@ struct Problem {
   int T;                 // chunks per sequence
   int score_blocks_per_group;  // score blocks per (KV head, sequence); each loops over chunks
   // workspace (no initial contents required: every call writes what it later reads)
-  double* stash;         // [B, H, nk] in-chunk inclusive prefix of exp(s - m_t)
+  double* stash;         // [B, H, stash_stride] in-chunk inclusive prefix of exp(s - m_t)
+  int64_t stash_stride;  // T * CHUNK: rows padded to whole chunks
   double* cmax;          // [B, H, T] chunk max m_t
   double* csum;          // [B, H, T] chunk sum-exp l_t
   double* cdf;           // [B, H, T+1] exclusive prefix of W_t = l_t exp(m_t - m*); cdf[T] = Z
@@ -210,6 +275,8 @@ struct Problem {
   float* partial;        // [B, Hkv, T, G, d] per-chunk sums of count * V (fp32, exact products)
   int32_t* idx;          // [B, H, S]
   int32_t* unique;       // [B, Hkv, T] distinct sampled keys of each chunk
+  uint32_t* sink;        // [B, Hkv, T] values of the cache-warming loads (never read)
+  int32_t* sync_err;     // [B, Hkv, T] per score block: 1 if an LDS handshake timed out
   double* prob;          // optional [B, H, nk]
 };
 

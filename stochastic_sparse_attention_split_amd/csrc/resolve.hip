@@ -61,15 +61,23 @@ __device__ inline int last_positive(const double* P, int len) {
   return 0;
 }
 
-template <int D, bool BF16, int GM>
+// PER > 0: the chunk CDF is computed here from the chunk statistics (T <= 64 * PER, the same arithmetic
+// as the chunk CDF kernel, so every block of a head sees the same edges); PER == 0: it is read from the
+// chunk CDF kernel's output. Wave w handles heads w and w + 4 of the group up to the key counts, so a
+// wave searches only the prefix rows it wrote itself.
+template <int D, bool BF16, int GM, int PER>
 __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
   using Pc = Piece<BF16>;
   constexpr int EPL = Pc::EPL;
   constexpr int LPR = D / EPL;          // lanes per V row
   constexpr int NRG = THREADS / LPR;    // row groups
   constexpr int NWAVE = THREADS / 64;
+  constexpr int HPW = (GM + NWAVE - 1) / NWAVE;  // heads per wave
   constexpr int NCW = GM / 2;           // 32-bit words of 16-bit per-head counts
   constexpr int CW = NCW + 1;           // padded stride of the per-key counters
+  constexpr int ROWB = D * (BF16 ? 2 : 4);
+  constexpr int PFL = ROWB >= 128 ? ROWB / 128 : 1;  // 128-byte lines per V row
+  constexpr int PERL = PER > 0 ? PER : 1;
   static_assert((size_t)NWAVE * GM * D * sizeof(float) <= (size_t)GM * CHUNK * sizeof(double),
                 "the cross-wave sums reuse the prefix tile");
 
@@ -77,8 +85,6 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
   __shared__ uint32_t cnt[CHUNK * CW];
   __shared__ int32_t lkey[CHUNK];
   __shared__ uint32_t lcnt[CHUNK][NCW];
-  __shared__ double hC0[GM], hC1[GM], hF[GM], hZ[GM], hU[GM];
-  __shared__ int hLo[GM], hN[GM], hLast[GM];
   __shared__ int wsum_i[NWAVE];
 
   const int t = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
@@ -89,32 +95,76 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
   const int64_t bh0 = (int64_t)b * p.H + h0;
   const int64_t n0 = (int64_t)t * CHUNK;
   const int len = (int)min((int64_t)CHUNK, p.nk - n0);
+  const size_t esz = BF16 ? 2 : 4;
+  const char* vbase = (const char*)p.V + esz * ((int64_t)b * p.batch_stride + n0 * p.seq_stride + (int64_t)kv * D);
+  const int64_t rstride = esz * p.seq_stride;
 
-  // ---- every load of the sampling phase at once: the prefix tile (head clamped to G-1, key clamped to
-  //      the chunk's last key, so every address is valid) and this chunk's interval of the chunk CDF
-  double pv[GM];
+  // ---- every load of the sampling phase at once (heads clamped to G - 1 and keys to the chunk's last
+  //      key, so every address is valid): this wave's prefix rows and its heads' chunk CDF inputs
+  double pv[HPW][4];
+  double cm[HPW][PERL], cl[HPW][PERL];
+  double e0[HPW], e1[HPW], eZ[HPW], eF[HPW];
+  int eL[HPW];
 #pragma unroll
-  for (int j = 0; j < GM; ++j) {
-    const int g = min(j, G - 1), k = min(tid, len - 1);
-    pv[j] = p.stash[(bh0 + g) * p.nk + n0 + k];
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int64_t bh = bh0 + min(wave + NWAVE * hh, G - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[hh][i] = p.stash[bh * p.stash_stride + n0 + min(4 * lane + i, len - 1)];
+    if constexpr (PER > 0) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int tt = min(lane * PER + j, T - 1);
+        cm[hh][j] = p.cmax[bh * T + tt];
+        cl[hh][j] = p.csum[bh * T + tt];
+      }
+    } else {
+      const double* cdf = p.cdf + bh * (T + 1);
+      e0[hh] = cdf[t];
+      e1[hh] = cdf[t + 1];
+      eZ[hh] = cdf[T];
+      eF[hh] = p.cscale[bh * T + t];
+      eL[hh] = p.lastpos[bh];
+    }
   }
-  const int hg = min(tid, G - 1);
-  const double* cdf = p.cdf + (bh0 + hg) * (T + 1);
-  const double c0 = cdf[t], c1 = cdf[t + 1], Z = cdf[T];
-  const double f = p.cscale[(bh0 + hg) * T + t];
-  const int lastc = p.lastpos[bh0 + hg];
-
-#pragma unroll
-  for (int j = 0; j < GM; ++j) Pt[j][tid] = pv[j];
   for (int i = tid; i < CHUNK * CW; i += THREADS) cnt[i] = 0u;
-  if (tid < G) {
-    const int g = tid;
-    hC0[g] = c0;
-    hC1[g] = c1;
-    hZ[g] = Z;
-    hF[g] = f;
-    hLast[g] = lastc;
-    hU[g] = p.mode == 2 ? uniform53(p.seed, 0u, (uint32_t)(h0 + g), (uint32_t)b, TAG_SYS) : 0.0;
+  __syncthreads();  // counters zeroed before any wave counts (does not wait for the loads above)
+
+  int jpf[HPW];  // a sampled key of each of this lane's heads (key 0 if none), for cache warming
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) jpf[hh] = 0;
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int g = wave + NWAVE * hh;
+    if (g >= G) break;  // wave-uniform
+    double c0, c1, Z, f;
+    int lastc;
+    if constexpr (PER > 0) {
+      ChunkCdf<PER> o;
+      chunk_cdf_wave<PER>(cm[hh], cl[hh], T, lane, o);
+      c0 = readlane_f64(pick<PER>(o.c, t % PER), t / PER);
+      c1 = t + 1 < T ? readlane_f64(pick<PER>(o.c, (t + 1) % PER), (t + 1) / PER) : o.top;
+      f = readlane_f64(pick<PER>(o.f, t % PER), t / PER);
+      Z = o.top;
+      lastc = o.last;
+    } else {
+      c0 = e0[hh];
+      c1 = e1[hh];
+      Z = eZ[hh];
+      f = eF[hh];
+      lastc = eL[hh];
+    }
+    // this head's prefix row, written and then searched by this wave only
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Pt[g][4 * lane + i] = pv[hh][i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    if (p.prob) {  // debug: probabilities of this chunk's keys from the score pass's exponentials
+      double* pr = p.prob + (bh0 + g) * p.nk + n0;
+      for (int k = lane; k < len; k += 64) pr[k] = pr[k] * f / Z;
+    }
+    const double u_sys = p.mode == 2 ? uniform53(p.seed, 0u, (uint32_t)(h0 + g), (uint32_t)b, TAG_SYS) : 0.0;
     int lo = 0, n = 0;
     if (c1 > c0 || t == lastc) {
       if (p.mode == 0) {
@@ -127,40 +177,30 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
         n = ihi >= ilo ? ihi - ilo + 1 : 0;
       }
     }
-    hLo[g] = lo;
-    hN[g] = n;
-  }
-  __syncthreads();
-
-  // debug: probabilities of this chunk's keys from the score pass's exponentials
-  if (p.prob) {
-    for (int i = tid; i < G * len; i += THREADS) {
-      const int g = i / len, k = i % len;
-      double* pr = p.prob + (bh0 + g) * p.nk + n0 + k;
-      *pr = *pr * hF[g] / hZ[g];
+    for (int c = lane; c < n; c += 64) {
+      const int m = lo + c;
+      const double y = point_of(p, m, h0 + g, b, u_sys) * Z;
+      const bool mine = y < Z ? (c0 <= y && y < c1) : (t == lastc);
+      if (!mine) continue;
+      int j;
+      if (y < Z) {
+        j = search_chunk(Pt[g], f, y - c0);
+        if (j < 0) j = last_positive(Pt[g], len);  // the residual reached the chunk total through rounding
+      } else {
+        j = last_positive(Pt[g], len);
+      }
+      p.idx[(bh0 + g) * S + m] = (int32_t)(n0 + j);
+      atomicAdd(&cnt[j * CW + (g >> 1)], (g & 1) ? 0x10000u : 1u);
+      jpf[hh] = j;
     }
   }
-
-  // ---- resolve the candidate points that land in this chunk and count them per key and head
-  int total = 0;
-  for (int g = 0; g < G; ++g) total += hN[g];
-  for (int c = tid; c < total; c += THREADS) {
-    int g = 0, off = c;
-    while (off >= hN[g]) off -= hN[g++];
-    const int m = hLo[g] + off;
-    const double y = point_of(p, m, h0 + g, b, hU[g]) * hZ[g];
-    const bool mine = y < hZ[g] ? (hC0[g] <= y && y < hC1[g]) : (t == hLast[g]);
-    if (!mine) continue;
-    int j;
-    if (y < hZ[g]) {
-      j = search_chunk(Pt[g], hF[g], y - hC0[g]);
-      if (j < 0) j = last_positive(Pt[g], len);  // the residual reached the chunk total through rounding
-    } else {
-      j = last_positive(Pt[g], len);
-    }
-    p.idx[(bh0 + g) * S + m] = (int32_t)(n0 + j);
-    atomicAdd(&cnt[j * CW + (g >> 1)], (g & 1) ? 0x10000u : 1u);
-  }
+  // warm the caches with rows the gather below will read; the values are consumed only at the very end,
+  // so nothing waits for these loads before the gather's own loads of the same lines
+  uint32_t warm[HPW][PFL];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+    for (int L = 0; L < PFL; ++L) warm[hh][L] = *(const uint32_t*)(vbase + jpf[hh] * rstride + L * 128);
   __syncthreads();
 
   // ---- compact the sampled keys (thread k owns key k)
@@ -201,9 +241,6 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
   for (int g = 0; g < GM; ++g)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
-  const size_t esz = BF16 ? 2 : 4;
-  const char* vbase = (const char*)p.V + esz * ((int64_t)b * p.batch_stride + n0 * p.seq_stride + (int64_t)kv * D);
-  const int64_t rstride = esz * p.seq_stride;
   for (int u0 = rg; u0 < nu; u0 += NRG * BATCH) {
     // list entries past nu re-read the last entry's row and are added with count 0
     int key[BATCH];
@@ -257,6 +294,12 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
     for (int w2 = 0; w2 < NWAVE; ++w2) s += wsum[((size_t)w2 * GM + g) * D + e];
     dst[i] = s;
   }
+  uint32_t sink = 0u;
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+    for (int L = 0; L < PFL; ++L) sink ^= warm[hh][L];
+  if (lane == 0) p.sink[(int64_t)grp * T + t] = sink;  // keeps the cache-warming loads
 }
 
 // out[b, h] = round((sum over chunks of the partials of head h) / S); fp64 sum in chunk order
@@ -309,16 +352,23 @@ __global__ __launch_bounds__(THREADS) void merge_kernel(Problem p) {
   }
 }
 
+template <int D, bool BF16, int GM>
+hipError_t launch_resolve_g(const Problem& p, hipStream_t st) {
+  const dim3 grid(p.T, p.Hkv, p.B);
+  if (p.T <= 64)
+    resolve_kernel<D, BF16, GM, 1><<<grid, THREADS, 0, st>>>(p);
+  else if (p.T <= FUSED_CDF_MAX_T)
+    resolve_kernel<D, BF16, GM, 2><<<grid, THREADS, 0, st>>>(p);
+  else
+    resolve_kernel<D, BF16, GM, 0><<<grid, THREADS, 0, st>>>(p);
+  return hipGetLastError();
+}
+
 template <int D, bool BF16>
 hipError_t launch_resolve_dt(const Problem& p, hipStream_t st) {
-  dim3 grid(p.T, p.Hkv, p.B);
-  if (p.G <= 2)
-    resolve_kernel<D, BF16, 2><<<grid, THREADS, 0, st>>>(p);
-  else if (p.G <= 4)
-    resolve_kernel<D, BF16, 4><<<grid, THREADS, 0, st>>>(p);
-  else
-    resolve_kernel<D, BF16, 8><<<grid, THREADS, 0, st>>>(p);
-  return hipGetLastError();
+  if (p.G <= 2) return launch_resolve_g<D, BF16, 2>(p, st);
+  if (p.G <= 4) return launch_resolve_g<D, BF16, 4>(p, st);
+  return launch_resolve_g<D, BF16, 8>(p, st);
 }
 
 }  // namespace

@@ -37,7 +37,7 @@ constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-  size_t stash, cmax, csum, cdf, cscale, lastpos, partial, idx, unique, total;
+  size_t stash, cmax, csum, cdf, cscale, lastpos, partial, idx, unique, sink, sync_err, total;
 };
 
 // every region is written by the call before it is read: no initial contents are required
@@ -51,7 +51,7 @@ Layout layout(int64_t B, int64_t nk, int64_t H, int64_t Hkv, int64_t d, int64_t 
     off = align_up(off + bytes);
     return at;
   };
-  L.stash = take((size_t)(B * H * nk) * sizeof(double));
+  L.stash = take((size_t)(B * H * T * CHUNK) * sizeof(double));
   L.cmax = take((size_t)(B * H * T) * sizeof(double));
   L.csum = take((size_t)(B * H * T) * sizeof(double));
   L.cdf = take((size_t)(B * H * (T + 1)) * sizeof(double));
@@ -60,6 +60,8 @@ Layout layout(int64_t B, int64_t nk, int64_t H, int64_t Hkv, int64_t d, int64_t 
   L.partial = take((size_t)(B * Hkv * T * G * d) * sizeof(float));
   L.idx = take((size_t)(B * H * S) * sizeof(int32_t));
   L.unique = take((size_t)(B * Hkv * T) * sizeof(int32_t));
+  L.sink = take((size_t)(B * Hkv * T) * sizeof(uint32_t));
+  L.sync_err = take((size_t)(B * Hkv * T) * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -182,6 +184,7 @@ int santa_decode_ex(const santa_args* a) {
   p.T = (int)((a->nk + CHUNK - 1) / CHUNK);
   p.score_blocks_per_group = score_blocks_per_group(p.B * p.Hkv, p.T, score_blocks_per_cu(p.d, p.bf16, p.G));
   p.stash = (double*)(ws + L.stash);
+  p.stash_stride = (int64_t)p.T * CHUNK;
   p.cmax = (double*)(ws + L.cmax);
   p.csum = (double*)(ws + L.csum);
   p.cdf = (double*)(ws + L.cdf);
@@ -190,6 +193,8 @@ int santa_decode_ex(const santa_args* a) {
   p.partial = (float*)(ws + L.partial);
   p.idx = a->idx_out ? a->idx_out : (int32_t*)(ws + L.idx);
   p.unique = (int32_t*)(ws + L.unique);
+  p.sink = (uint32_t*)(ws + L.sink);
+  p.sync_err = (int32_t*)(ws + L.sync_err);
   p.prob = a->prob_out;
 
   hipStream_t stream = (hipStream_t)a->stream;
@@ -206,7 +211,8 @@ int santa_decode_ex(const santa_args* a) {
   (void)hipGetLastError();  // start from a clean error state
   if ((e = launch_score(p, stream)) != hipSuccess) return hip_fail(e, "score kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  if ((e = launch_chunk_cdf(p, stream)) != hipSuccess) return hip_fail(e, "chunk CDF kernel launch");
+  const bool cdf_kernel = p.T > FUSED_CDF_MAX_T;  // otherwise the sampling kernel builds the chunk CDF
+  if (cdf_kernel && (e = launch_chunk_cdf(p, stream)) != hipSuccess) return hip_fail(e, "chunk CDF kernel launch");
   if ((e = launch_resolve(p, stream)) != hipSuccess) return hip_fail(e, "resolve kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if ((e = launch_merge(p, stream)) != hipSuccess) return hip_fail(e, "merge kernel launch");
@@ -220,9 +226,16 @@ int santa_decode_ex(const santa_args* a) {
     if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
     int64_t U = 0;
     for (int32_t x : u) U += x;
+    if (p.bf16 && p.G <= 4) {  // the streaming score kernel flags a timed-out LDS handshake per block
+      std::vector<int32_t> fl((size_t)p.score_blocks_per_group * p.Hkv * p.B);
+      if ((e = hipMemcpy(fl.data(), p.sync_err, fl.size() * sizeof(int32_t), hipMemcpyDeviceToHost)) != hipSuccess)
+        return hip_fail(e, "hipMemcpy(sync flags)");
+      for (int32_t x : fl)
+        if (x != 0) return fail(SANTA_ERR_HIP, "score kernel: an LDS handshake timed out (%d)", x);
+    }
     const int64_t esz = p.bf16 ? 2 : 4;
     santa_stats* s = a->stats_out;
-    s->launches = 4;
+    s->launches = cdf_kernel ? 4 : 3;
     s->bytes_k = (int64_t)a->batch * a->nk * a->kv_heads * a->d * esz;
     s->bytes_v = U * a->d * esz;
     s->bytes_qo = 2 * (int64_t)a->batch * a->heads * a->d * esz;

@@ -97,60 +97,27 @@ __global__ __launch_bounds__(THREADS) void chunk_cdf_reg_kernel(Problem p) {
   const int t0 = lane * PER;
   for (int g = wave; g < p.G; g += THREADS / 64) {
     const int64_t bh = (int64_t)b * p.H + h0 + g;
-    const double* cm = p.cmax + bh * T;
-    const double* cs = p.csum + bh * T;
     double m[PER], l[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int tt = min(t0 + j, T - 1);  // every lane loads a valid address; extra entries are masked
-      m[j] = cm[tt];
-      l[j] = cs[tt];
+      m[j] = p.cmax[bh * T + tt];
+      l[j] = p.csum[bh * T + tt];
     }
-    double mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if (t0 + j < T) mx = fmax(mx, m[j]);
-    const double ms = readlane_f64(wave_incl_max_dpp(mx), 63);
-    double f[PER], loc[PER], run = 0.0;
-    int lp = -1;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const bool valid = t0 + j < T;
-      f[j] = valid ? exp(m[j] - ms) : 0.0;
-      const double w = l[j] * f[j];
-      loc[j] = run;  // local exclusive prefix, offset below
-      run += w;
-      if (valid && w > 0.0) lp = t0 + j;
-    }
-    const double incl = wave_incl_scan_dpp(run);
-    double excl = __shfl_up(incl, 1, 64);
-    if (lane == 0) excl = 0.0;
-    double lmax = 0.0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const double c = fmax(excl + loc[j], lmax);
-      loc[j] = c;
-      lmax = c;
-    }
-    // running maximum across lanes: lane l's values are raised to the maximum of all earlier lanes
-    const double pmax = wave_incl_max_dpp(t0 < T ? lmax : 0.0);
-    double before = __shfl_up(pmax, 1, 64);
-    if (lane == 0) before = 0.0;
+    ChunkCdf<PER> o;
+    chunk_cdf_wave<PER>(m, l, T, lane, o);
     double* cdf = p.cdf + bh * (T + 1);
     double* csc = p.cscale + bh * T;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       if (t0 + j < T) {
-        cdf[t0 + j] = fmax(loc[j], before);
-        csc[t0 + j] = f[j];
+        cdf[t0 + j] = o.c[j];
+        csc[t0 + j] = o.f[j];
       }
     }
-    const double Z = readlane_f64(incl, 63);
-    const double top = readlane_f64(pmax, 63);
-    const double lpd = readlane_f64(wave_incl_max_dpp((double)lp), 63);
     if (lane == 0) {
-      cdf[T] = fmax(Z, top);
-      p.lastpos[bh] = (int32_t)lpd;
+      cdf[T] = o.top;
+      p.lastpos[bh] = o.last;
     }
   }
 }
@@ -291,7 +258,7 @@ __global__ __launch_bounds__(THREADS, MINB) void score_kernel(Problem p) {
       const int g = wave + 4 * j;
       if (g >= G) break;
       const int64_t bh = (int64_t)b * p.H + h0 + g;
-      double* dst = p.stash + bh * p.nk + pend_n0;
+      double* dst = p.stash + bh * p.stash_stride + pend_n0;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (4 * lane + i < pend_len) dst[4 * lane + i] = pend[j][i];
@@ -400,6 +367,322 @@ __global__ __launch_bounds__(THREADS, MINB) void score_kernel(Problem p) {
   flush();
 }
 
+// ---------------------------------------------------------------------------------------------
+// Streaming form for bf16 caches (one block per CU). The memory system copies each chunk's K tile
+// straight into LDS (global_load_lds: 16 bytes per lane, no register staging), two tiles in flight: the
+// copy of chunk k+2 starts as soon as chunk k's matrix-core pass has finished reading its tile, so the
+// HBM stream does not pause for the exponentials and stores. The compiler does not track these copies;
+// the block waits for them with explicit vmcnt waits whose counts are derived in the loop below.
+
+// the LDS address of a __shared__ object, as the 32-bit offset M0 takes
+__device__ inline uint32_t lds_addr(const void* ptr) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ptr;
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// one wave-wide copy global -> LDS: lane l's 16 bytes at `g` land at LDS address lds + 16 l
+__device__ inline void copy_to_lds16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ inline void wait_vm() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if constexpr (N == 32) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+  else if constexpr (N == 64) asm volatile("s_waitcnt vmcnt(63)" ::: "memory");
+  else static_assert(N == 0, "unsupported count");
+}
+
+constexpr int SMFMA = 4;                 // matrix-core waves: 64 keys each, one per SIMD
+constexpr int SSOFT = 4;                 // exponential waves: one head each
+constexpr int SCOPY = 4;                 // copy waves: two per K tile
+constexpr int STHREADS = 64 * (SMFMA + SSOFT + SCOPY);
+constexpr int SPIN_LIMIT = 1 << 22;      // bounded waits: a stuck handshake ends the kernel, flagged
+
+template <int D>
+struct SGeo {
+  static constexpr int ROWB = D * 2;         // bytes per bf16 K row
+  static constexpr int PPR = ROWB / 16;      // 16-byte pieces per row (16 or 8)
+  static constexpr int TILE = CHUNK * ROWB;  // bytes per chunk tile (64 or 32 KiB)
+  static constexpr int CPW = TILE / 1024 / 2;  // wave-wide 1 KiB copies per copy wave per chunk (32 or 16)
+  static constexpr int RPS = 1024 / ROWB;    // rows per 1 KiB copy (4 or 8)
+  static constexpr int PP = PPR / 4;         // pieces per lane per row in the matrix-core layout
+};
+
+// byte offset of piece `pc` of row `row` in a tile: pieces are XOR-swizzled by the row, so the 16 rows a
+// quarter-wave reads in the matrix-core layout fall in distinct LDS banks
+template <int D>
+__device__ inline int tile_off(int row, int pc) {
+  return row * SGeo<D>::ROWB + ((pc ^ (row % SGeo<D>::PPR)) << 4);
+}
+
+// LDS handshake counters. signal(): this wave's earlier LDS writes (and, for copy waves, the copies
+// waited for) are complete, then one lane adds 1. wait_ge(): poll until the counter reaches `target`;
+// false after SPIN_LIMIT polls (the caller then abandons the block and flags it).
+__device__ inline void signal(int* ctr, int lane) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ inline bool wait_ge(int* ctr, int target) {
+  int spins = 0;
+  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+    if (++spins > SPIN_LIMIT) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+  return true;
+}
+
+// Streaming score pass for bf16 caches and G <= 4, one block per CU, three roles that meet only through
+// LDS counters (no block-wide barrier after the start), so the K stream, the matrix cores and the
+// exponentials overlap:
+//   * waves 0..3 (one per SIMD): fp64 MFMA over 64 keys each (four 16-key groups; the head dimension
+//     split by element parity gives eight independent accumulation chains) into the score buffer of the
+//     chunk's parity;
+//   * waves 4..7: chunk max, exponentials, in-chunk prefix and the stores of head w - 4;
+//   * waves 8..11: global -> LDS copies (global_load_lds) of the K tiles, waves 8-9 tile 0 with the
+//     block's even chunks, 10-11 tile 1 with the odd ones (wave 10 first copies the queries).
+// Counters (chunk k lives in tile k & 1 and score buffer k & 1; its fill index there is k >> 1):
+//   ld[j] +1 per copy wave when its half of tile j's current chunk has landed;
+//   use[j] +1 per MFMA wave when its reads of tile j are done;  md +1 per MFMA wave per chunk scored;
+//   sd +1 per exponential wave per chunk finished;  qr queries landed;  pb prologue barrier;
+//   fin waves finished (the last one publishes the block's handshake status).
+template <int D>
+__global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
+  using Sg = SGeo<D>;
+  constexpr int EPL = 8, PP = Sg::PP, CPW = Sg::CPW;
+  constexpr int KPW = CHUNK / SMFMA;  // keys per MFMA wave
+  constexpr int NGR = KPW / 16;       // 16-key groups per MFMA wave
+  static_assert(D * 2 * 4 <= 1024, "the queries of a group fit one 1 KiB copy");
+
+  __shared__ __align__(16) unsigned char kt[2][Sg::TILE];
+  __shared__ __align__(16) double sc[2][4][CHUNK];
+  __shared__ __align__(16) double qe[4][D + 2];
+  __shared__ double hnorm[4];
+  __shared__ __align__(16) unsigned char qs[1024];
+  __shared__ int ctr[10];
+  int* ld = &ctr[0];   // [2]
+  int* use = &ctr[2];  // [2]
+  int* md = &ctr[4];
+  int* sd = &ctr[5];
+  int* qr = &ctr[6];
+  int* pb = &ctr[7];
+  int* fin = &ctr[8];
+  int* bad = &ctr[9];
+
+  const int kv = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = p.G;
+  const int h0 = kv * G;
+  const int T = p.T;
+  const int step = gridDim.x;
+  const int t0 = blockIdx.x;
+  if (t0 >= T) return;
+  const int n = (T - 1 - t0) / step + 1;  // this block's chunks: t0, t0 + step, ...
+  int* err = p.sync_err + ((int64_t)b * gridDim.y + kv) * gridDim.x + t0;
+
+  if (tid < 10) ctr[tid] = 0;
+  __syncthreads();  // the only block-wide barrier
+
+  const int64_t seq_bytes = 2 * p.seq_stride;
+  const char* kbase = (const char*)p.K + 2 * ((int64_t)b * p.batch_stride + (int64_t)kv * D);
+  auto chunk_len = [&](int tt) { return (int)min((int64_t)CHUNK, p.nk - (int64_t)tt * CHUNK); };
+  bool ok = true;
+  // every wave ends here: the last one to finish publishes whether any handshake timed out
+  auto finish = [&]() {
+    if (lane == 0) {
+      if (!ok) __hip_atomic_fetch_or(bad, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const int before = __hip_atomic_fetch_add(fin, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (before == STHREADS / 64 - 1)
+        __hip_atomic_store(err, __hip_atomic_load(bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+
+  if (wave >= SMFMA + SSOFT) {
+    // ---- copy waves: at most one chunk's copies in flight per wave, so vmcnt(0) means all landed.
+    // Highest issue priority on their SIMD: they issue rarely and the whole block waits on them.
+    __builtin_amdgcn_s_setprio(3);
+    const int j = (wave - SMFMA - SSOFT) >> 1, hf = (wave - SMFMA - SSOFT) & 1;
+    if (j == 1 && hf == 0) {
+      const char* qsrc = (const char*)p.q + ((int64_t)b * p.H + h0) * D * 2;
+      copy_to_lds16(qsrc + min(lane * 16, G * D * 2 - 16), lds_addr(qs));
+      wait_vm<0>();
+      signal(qr, lane);
+    }
+    for (int k = j, m = 0; k < n && ok; k += 2, ++m) {
+      if (m > 0) ok = wait_ge(&use[j], SMFMA * m);  // the tile's previous chunk is no longer read
+      if (!ok) break;
+      const int t = t0 + k * step;
+      const int64_t n0 = (int64_t)t * CHUNK;
+      const int len = chunk_len(t);
+      const uint32_t base = lds_addr(&kt[j][0]);
+#pragma unroll 4
+      for (int i = 0; i < CPW; ++i) {
+        const int q = hf * CPW + i;
+        const int row = q * Sg::RPS + lane / Sg::PPR;
+        const int pc = (lane % Sg::PPR) ^ (row % Sg::PPR);
+        const int grow = row < len ? row : 0;  // rows past the end re-read row 0 (masked later)
+        copy_to_lds16(kbase + (n0 + grow) * seq_bytes + pc * 16, base + q * 1024);
+      }
+      wait_vm<0>();
+      signal(&ld[j], lane);
+    }
+    wait_vm<0>();  // no copy may land after the block ends
+    finish();
+    return;
+  }
+
+  // ---- prologue of the MFMA and exponential waves (12 waves, counter barrier pb)
+  int np = 0;
+  auto pbar = [&]() {
+    signal(pb, lane);
+    ++np;
+    ok = ok && wait_ge(pb, (SMFMA + SSOFT) * np);
+  };
+  ok = wait_ge(qr, 1);
+  if (ok) {
+    for (int i = tid; i < 4 * D; i += (SMFMA + SSOFT) * 64) {
+      const int g = i / D, e = i % D;
+      double v = 0.0;
+      if (g < G) v = (double)__uint_as_float(((uint32_t)((const uint16_t*)qs)[g * D + e]) << 16);
+      qe[g][e] = v;
+    }
+  }
+  pbar();
+  if (p.ternary) {
+    if (ok && tid < 4) {
+      double m = 0.0;
+      for (int e = 0; e < D; ++e) m = fmax(m, fabs(qe[tid][e]));
+      hnorm[tid] = m;
+    }
+    pbar();
+    if (ok) {
+      for (int i = tid; i < 4 * D; i += (SMFMA + SSOFT) * 64) {
+        const int g = i / D, e = i % D;
+        const double v = qe[g][e];
+        const double nrm = hnorm[g];
+        double rr = 0.0;
+        if (g < G && nrm > 0.0) {
+          const double u = uniform53(p.seed, (uint32_t)e, (uint32_t)(h0 + g), (uint32_t)b, TAG_BERNOULLI);
+          if (u < fabs(v) / nrm) rr = v > 0.0 ? 1.0 : (v < 0.0 ? -1.0 : 0.0);
+        }
+        qe[g][e] = rr;
+      }
+    }
+    pbar();
+  }
+
+  if (wave >= SMFMA) {
+    // ---- exponential waves: head g of every chunk, lane owns keys 4*lane .. 4*lane + 3. Issue priority
+    // above the MFMA waves sharing their SIMD, whose instruction stream would otherwise starve them.
+    __builtin_amdgcn_s_setprio(2);
+    const int g = wave - SMFMA;
+    const bool act = g < G;  // wave-uniform
+    const double nrm = p.ternary && act ? hnorm[g] : 1.0;
+    const int64_t bh = (int64_t)b * p.H + h0 + (act ? g : 0);
+    for (int k = 0; k < n && ok; ++k) {
+      ok = wait_ge(md, SMFMA * (k + 1));  // chunk k's scores are complete
+      if (!ok) break;
+      if (act) {
+        const int t = t0 + k * step;
+        const int len = chunk_len(t);
+        const int64_t n0 = (int64_t)t * CHUNK;
+        const double* row = &sc[k & 1][g][0];
+        double sv[4];
+        double lmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = 4 * lane + i;
+          double v = row[kk];
+          if (p.ternary) v = v * nrm;  // (qhat . K) * norm, then * (1/sqrt(dk))
+          v = v * p.scale;
+          sv[i] = kk < len ? v : -INFINITY;
+          lmax = fmax(lmax, sv[i]);
+        }
+        const double m = readlane_f64(wave_incl_max_dpp(lmax), 63);
+        double ex[4], pre[4], run = 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ex[i] = (4 * lane + i) < len ? exp(sv[i] - m) : 0.0;
+          run += ex[i];
+          pre[i] = run;
+        }
+        const double incl = wave_incl_scan_dpp(run);
+        double excl = __shfl_up(incl, 1, 64);
+        if (lane == 0) excl = 0.0;
+        signal(sd, lane);  // the score buffer has been read
+        // stash rows are CHUNK-padded: the whole chunk is stored, keys past the end repeat the total
+        double2* dst = (double2*)(p.stash + bh * p.stash_stride + n0 + 4 * lane);
+        dst[0] = make_double2(excl + pre[0], excl + pre[1]);
+        dst[1] = make_double2(excl + pre[2], excl + pre[3]);
+        if (lane == 0) {
+          p.cmax[bh * T + t] = m;
+          p.csum[bh * T + t] = readlane_f64(incl, 63);
+        }
+        if (p.prob) {
+          double* pr = p.prob + bh * p.nk + n0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * lane + i < len) pr[4 * lane + i] = ex[i];
+        }
+      } else {
+        signal(sd, lane);
+      }
+    }
+    finish();
+    return;
+  }
+
+  // ---- MFMA waves: 16-key groups x element parity = independent accumulation chains
+  const int slot = lane >> 4;
+  double qb[PP][EPL];
+#pragma unroll
+  for (int pp = 0; pp < PP; ++pp)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qb[pp][e] = qe[lane & 3][EPL * (4 * pp + slot) + e];
+  for (int k = 0; k < n && ok; ++k) {
+    ok = wait_ge(&ld[k & 1], 2 * ((k >> 1) + 1));  // chunk k's tile has landed
+    if (!ok) break;
+    const unsigned char* ks = &kt[k & 1][0];
+    double acc[NGR][2];  // [group][element parity]
+#pragma unroll
+    for (int gi = 0; gi < NGR; ++gi) acc[gi][0] = acc[gi][1] = 0.0;
+#pragma unroll
+    for (int pp = 0; pp < PP; ++pp) {
+      uint4 a4[NGR];
+#pragma unroll
+      for (int gi = 0; gi < NGR; ++gi)
+        a4[gi] = *(const uint4*)(ks + tile_off<D>(wave * KPW + gi * 16 + (lane & 15), 4 * pp + slot));
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+#pragma unroll
+        for (int gi = 0; gi < NGR; ++gi)
+          acc[gi][e & 1] = __builtin_amdgcn_mfma_f64_4x4x4f64(piece_elem<true>(a4[gi], e), qb[pp][e],
+                                                               acc[gi][e & 1], 0, 0, 0);
+    }
+    signal(&use[k & 1], lane);  // this wave's reads of tile k & 1 are complete
+    if (k >= 2) ok = wait_ge(sd, SSOFT * (k - 1));  // score buffer k & 1 was read for chunk k - 2
+    if (!ok) break;
+#pragma unroll
+    for (int gi = 0; gi < NGR; ++gi) {
+      const int key = wave * KPW + gi * 16 + 4 * ((lane >> 2) & 3) + (lane >> 4);
+      sc[k & 1][lane & 3][key] = acc[gi][0] + acc[gi][1];
+    }
+    signal(md, lane);
+  }
+  finish();
+}
+
 template <int D, bool BF16, int NQ>
 constexpr int blocks_per_cu() {
   constexpr size_t lds = (size_t)Geo<D, BF16>::LDS_K + 4 * NQ * CHUNK * sizeof(double) + 4 * NQ * sizeof(double);
@@ -415,12 +698,19 @@ hipError_t launch_q(const Problem& p, hipStream_t st) {
 
 template <int D, bool BF16>
 hipError_t launch_d(const Problem& p, hipStream_t st) {
+  if constexpr (BF16) {
+    if (p.G <= 4) {
+      score_stream_kernel<D><<<dim3(p.score_blocks_per_group, p.Hkv, p.B), STHREADS, 0, st>>>(p);
+      return hipGetLastError();
+    }
+  }
   return p.G <= 4 ? launch_q<D, BF16, 1>(p, st) : launch_q<D, BF16, 2>(p, st);
 }
 
 }  // namespace
 
 int score_blocks_per_cu(int d, bool bf16, int G) {
+  if (bf16 && G <= 4) return 1;  // streaming form: one block per CU (two K tiles fill most of the LDS)
   const bool q1 = G <= 4;
   if (d == 128) {
     if (bf16) return q1 ? blocks_per_cu<128, true, 1>() : blocks_per_cu<128, true, 2>();

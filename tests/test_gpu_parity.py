@@ -52,6 +52,8 @@ SMALL = [
     (1, 6, 2, 128, 1300, "bf16", "strat", 50, False, 3),   # G = 3 (group tile wider than the group)
     (1, 5, 1, 64, 900, "bf16", "iid", 20, False, 2),       # G = 5
     (1, 6, 1, 128, 1800, "f32", "sys", 40, False, 2),      # G = 6, fp32
+    (1, 16, 2, 64, 20000, "bf16", "strat", 100, False, 4),  # 79 chunks: chunk CDF built in the sampling kernel
+    (1, 8, 1, 128, 30000, "bf16", "iid", 64, False, 3),     # 118 chunks, G = 8
 ]
 
 
