@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--profile-steps", action="store_true", help="minimal run for profilers: no CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 5 plain 64 MiB device copies (scale reference for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -190,6 +192,15 @@ def main():
         dmed = statistics.median(dense_us)
         res["dense_bf16_us_median"] = round(dmed, 3)
         res["speedup_vs_dense"] = round(dmed / med, 3)
+
+    if args.copy_calibration:
+        src = torch.ones((64 << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            thrash.add_(1.0)
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = {"read": 64 << 20, "write": 64 << 20, "copies": 5}
 
     if not args.no_cpu_baseline and not args.profile_steps:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
