@@ -9,5 +9,6 @@ from .santa import (IID, STRAT, SYS, TERNARY_Q, MODE_NAMES, DecodeResult, bytes_
                     estimate, inverse_cdf, round_to_bf16, round_to_f32, sample_points, scale, scores_exact,
                     scores_ternary, softmax, stratum_weights, ternary_query, var_trace_iid, var_trace_strat)
 from . import philox
+from . import prop
 
 MODES = {"iid": IID, "strat": STRAT, "sys": SYS}

@@ -432,11 +432,27 @@ __device__ inline void signal(int* ctr, int lane) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+// A polling wave drops to the lowest issue priority while it waits (its polls would otherwise take issue
+// slots from the MFMA waves sharing its SIMD) and returns to `prio` once the counter is reached.
+template <int PRIO = 0>
 __device__ inline bool wait_ge(int* ctr, int target) {
   int spins = 0;
+  bool low = false;
   while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
-    if (++spins > SPIN_LIMIT) return false;
-    __builtin_amdgcn_s_sleep(1);
+    if (++spins > SPIN_LIMIT) {
+      if (low) __builtin_amdgcn_s_setprio(PRIO);
+      return false;
+    }
+    if constexpr (PRIO > 0) {
+      if (!low) {
+        __builtin_amdgcn_s_setprio(0);
+        low = true;
+      }
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  if constexpr (PRIO > 0) {
+    if (low) __builtin_amdgcn_s_setprio(PRIO);
   }
   asm volatile("" ::: "memory");
   return true;
@@ -520,7 +536,7 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
       signal(qr, lane);
     }
     for (int k = j, m = 0; k < n && ok; k += 2, ++m) {
-      if (m > 0) ok = wait_ge(&use[j], SMFMA * m);  // the tile's previous chunk is no longer read
+      if (m > 0) ok = wait_ge<3>(&use[j], SMFMA * m);  // the tile's previous chunk is no longer read
       if (!ok) break;
       const int t = t0 + k * step;
       const int64_t n0 = (int64_t)t * CHUNK;
@@ -591,7 +607,7 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
     const double nrm = p.ternary && act ? hnorm[g] : 1.0;
     const int64_t bh = (int64_t)b * p.H + h0 + (act ? g : 0);
     for (int k = 0; k < n && ok; ++k) {
-      ok = wait_ge(md, SMFMA * (k + 1));  // chunk k's scores are complete
+      ok = wait_ge<2>(md, SMFMA * (k + 1));  // chunk k's scores are complete
       if (!ok) break;
       if (act) {
         const int t = t0 + k * step;
