@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-prop", action="store_true", help="skip the S2ANTA-prop (S=128) measurement")
     ap.add_argument("--profile-steps", action="store_true", help="minimal run for profilers: no CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 64 MiB device copies (scale reference for hardware byte counters)")
@@ -130,6 +131,15 @@ def main():
     stage = np.array(stage) * 1e3  # us
     score_us = float(np.mean(stage[:, 0]))
 
+    prop_us = None
+    if not args.no_prop:  # S²ANTA-prop at the paper's 32k operating point (S = 128), same protocol
+        def prop_step():
+            santa.decode(q, K, V, 128, "prop", w.seed, ternary=ternary, out=out, workspace=ws, stream=stream)
+
+        for _ in range(args.warmup):
+            prop_step()
+        prop_us = timed(prop_step, args.steps, cold=True)
+
     dense_us = None
     if not args.no_dense:
         for _ in range(args.warmup):
@@ -192,6 +202,11 @@ def main():
         dmed = statistics.median(dense_us)
         res["dense_bf16_us_median"] = round(dmed, 3)
         res["speedup_vs_dense"] = round(dmed / med, 3)
+    if prop_us is not None:
+        pmed = statistics.median(prop_us)
+        res["s2anta_prop_S128"] = {"us_median": round(pmed, 3), "us_mean": round(statistics.fmean(prop_us), 3)}
+        if dense_us is not None:
+            res["s2anta_prop_S128"]["speedup_vs_dense"] = round(statistics.median(dense_us) / pmed, 3)
 
     if args.copy_calibration:
         src = torch.ones((64 << 20) // 4, dtype=torch.float32, device=dev)

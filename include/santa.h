@@ -55,6 +55,12 @@ extern "C" {
 #define SANTA_IID 0                 /* SANTA: T_m ~ U[0,1) i.i.d. (Section 2, Eq. 4) */
 #define SANTA_STRAT 1               /* S²ANTA-strat: T_m ~ U[m/S, (m+1)/S) independently (Section 2.1) */
 #define SANTA_SYS 2                 /* S²ANTA-sys: one U ~ U[0, 1/S), T_m = U + m/S (Section 2.1) */
+#define SANTA_PROP 3                /* S²ANTA-prop (Section 3.2; Appendix O, Algorithms 2-5): 256-key tiles get
+                                       largest-remainder budgets S_t ~ S W_t / Z, then systematic counts
+                                       c_n = floor(a0 + p + x_n) - floor(a0 + p) within the tile, with
+                                       x_n = S_t exp(s_n - m_t) / l_t and a0 ~ U(0,1) per (tile, head) from
+                                       Philox counter (t, h, b, 3). idx_out lists each head's sampled keys in
+                                       increasing order with multiplicity. */
 #define SANTA_TERNARY_Q 0x100       /* Bernoulli ternary query for the score stage (Section 5, Eq. 5; B = 1,
                                        norm = max_i |q_i| per (batch, head)) */
 
@@ -83,7 +89,7 @@ typedef struct santa_args {
   int64_t kv_seq_stride;     /* elements between consecutive positions; 0 means kv_heads * d */
   int64_t kv_batch_stride;   /* elements between sequences; 0 means nk * kv_seq_stride */
   int32_t S;                 /* samples per query head, >= 1 */
-  int32_t mode;              /* SANTA_IID | SANTA_STRAT | SANTA_SYS, optionally | SANTA_TERNARY_Q */
+  int32_t mode;              /* SANTA_IID | SANTA_STRAT | SANTA_SYS | SANTA_PROP, optionally | SANTA_TERNARY_Q */
   int32_t dtype;             /* SANTA_BF16 or SANTA_F32 */
   int32_t reserved0;
   uint64_t seed;

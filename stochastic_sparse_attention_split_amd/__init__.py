@@ -26,10 +26,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsanta.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-IID, STRAT, SYS = 0, 1, 2
+IID, STRAT, SYS, PROP = 0, 1, 2, 3
 TERNARY_Q = 0x100
 BF16, F32 = 0, 1
-MODES = {"iid": IID, "strat": STRAT, "sys": SYS}
+MODES = {"iid": IID, "strat": STRAT, "sys": SYS, "prop": PROP}
 
 EXPORTED = [
     "santa_decode", "santa_decode_ex", "santa_workspace_bytes", "santa_dense_decode",

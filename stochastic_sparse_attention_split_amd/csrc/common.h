@@ -54,6 +54,7 @@ __host__ __device__ inline double uniform53(uint64_t seed, uint32_t m, uint32_t 
 
 constexpr uint32_t TAG_POINT = 0;      // i.i.d. / stratified point m
 constexpr uint32_t TAG_SYS = 1;        // systematic offset (m = 0)
+constexpr uint32_t TAG_PROP = 3;       // S²ANTA-prop tile offset a0
 constexpr uint32_t TAG_BERNOULLI = 2;  // ternary-query element m (+256 n for Bernoulli sample n)
 
 // ---------------------------------------------------------------------------------------------
@@ -277,6 +278,8 @@ struct Problem {
   int32_t* unique;       // [B, Hkv, T] distinct sampled keys of each chunk
   uint32_t* sink;        // [B, Hkv, T] values of the cache-warming loads (never read)
   int32_t* sync_err;     // [B, Hkv, T] per score block: 1 if an LDS handshake timed out
+  int32_t* budget;       // [B, H, T] S²ANTA-prop tile budgets S_t
+  int32_t* boff;         // [B, H, T] exclusive prefix of the budgets (first idx slot of each tile)
   double* prob;          // optional [B, H, nk]
 };
 

@@ -10,6 +10,7 @@ namespace santa {
 hipError_t launch_score(const Problem& p, hipStream_t st);     // score.hip
 int score_blocks_per_cu(int d, bool bf16, int G);              // resident score blocks per CU (LDS)
 hipError_t launch_chunk_cdf(const Problem& p, hipStream_t st); // score.hip
+hipError_t launch_budget(const Problem& p, hipStream_t st);    // prop.hip: S²ANTA-prop tile budgets
 hipError_t launch_resolve(const Problem& p, hipStream_t st);   // resolve.hip: sample + gather per chunk
 hipError_t launch_merge(const Problem& p, hipStream_t st);     // resolve.hip: sum of the chunk partials
 

@@ -61,6 +61,121 @@ __device__ inline int last_positive(const double* P, int len) {
   return 0;
 }
 
+// Compaction of the keys counted in `cnt` (16-bit per-head counts, thread k owns key k), gather of their
+// V rows (each row once for the whole group, count * V into fp32 accumulators), and the chunk's partial
+// sums per head (App. O, Algorithm 5, lines 11-14). Ends with every thread past a barrier; `Pt` is reused
+// for the cross-wave sums.
+template <int D, bool BF16, int GM>
+__device__ inline void chunk_gather(const Problem& p, int t, int kv, int b, int len, uint32_t* cnt,
+                                    int32_t* lkey, uint32_t (*lcnt)[GM / 2], int* wsum_i, double (*Pt)[CHUNK]) {
+  using Pc = Piece<BF16>;
+  constexpr int EPL = Pc::EPL;
+  constexpr int LPR = D / EPL;          // lanes per V row
+  constexpr int NRG = THREADS / LPR;    // row groups
+  constexpr int NWAVE = THREADS / 64;
+  constexpr int NCW = GM / 2;
+  constexpr int CW = NCW + 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = p.G, T = p.T;
+  const int grp = b * p.Hkv + kv;
+  const int64_t n0 = (int64_t)t * CHUNK;
+  const size_t esz = BF16 ? 2 : 4;
+  const char* vbase = (const char*)p.V + esz * ((int64_t)b * p.batch_stride + n0 * p.seq_stride + (int64_t)kv * D);
+  const int64_t rstride = esz * p.seq_stride;
+  (void)len;
+  // ---- compact the sampled keys (thread k owns key k)
+  uint32_t mycw[NCW];
+  bool any = false;
+#pragma unroll
+  for (int w = 0; w < NCW; ++w) {
+    mycw[w] = cnt[tid * CW + w];
+    any |= mycw[w] != 0u;
+  }
+  const uint64_t bal = __ballot(any);
+  if (lane == 0) wsum_i[wave] = __popcll(bal);
+  __syncthreads();
+  int before = 0, nu = 0;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    if (w < wave) before += wsum_i[w];
+    nu += wsum_i[w];
+  }
+  if (any) {
+    const int pos = before + __popcll(bal & ((1ull << lane) - 1ull));
+    lkey[pos] = tid;
+#pragma unroll
+    for (int w = 0; w < NCW; ++w) lcnt[pos][w] = mycw[w];
+  }
+  if (tid == 0) p.unique[(int64_t)grp * T + t] = nu;
+  float* dst = p.partial + ((int64_t)grp * T + t) * G * D;
+  if (nu == 0) {  // block-uniform: nothing sampled here
+    for (int i = tid; i < G * D; i += THREADS) dst[i] = 0.0f;
+    return;
+  }
+  __syncthreads();
+
+  // ---- gather: each listed row once, added with its per-head counts
+  const int rg = tid / LPR, pc = tid % LPR;
+  float acc[GM][EPL];
+#pragma unroll
+  for (int g = 0; g < GM; ++g)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
+  for (int u0 = rg; u0 < nu; u0 += NRG * BATCH) {
+    // list entries past nu re-read the last entry's row and are added with count 0
+    int key[BATCH];
+    uint32_t cw[BATCH][NCW];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int u = u0 + k * NRG;
+      const int uu = min(u, nu - 1);
+      key[k] = lkey[uu];
+#pragma unroll
+      for (int w = 0; w < NCW; ++w) cw[k][w] = u < nu ? lcnt[uu][w] : 0u;
+    }
+    uint4 w4[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) w4[k] = load_stream16((const uint4*)(vbase + key[k] * rstride) + pc);
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      float v[EPL];
+      Pc::to_f32(w4[k], v);
+#pragma unroll
+      for (int g = 0; g < GM; ++g) {
+        const uint32_t c32 = cw[k][g >> 1];
+        const float c = (float)((g & 1) ? (c32 >> 16) : (c32 & 0xFFFFu));
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] += c * v[e];
+      }
+    }
+  }
+  // reduce the row groups: inside the wave by lane permutes, then across waves in LDS
+#pragma unroll
+  for (int g = 0; g < GM; ++g)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float x = acc[g][e];
+#pragma unroll
+      for (int o = LPR; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
+      acc[g][e] = x;
+    }
+  float* wsum = reinterpret_cast<float*>(&Pt[0][0]);  // [NWAVE][GM][D]; Pt is dead after the last sync
+  if (lane < LPR) {
+#pragma unroll
+    for (int g = 0; g < GM; ++g)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) wsum[((size_t)wave * GM + g) * D + pc * EPL + e] = acc[g][e];
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += THREADS) {
+    const int g = i / D, e = i % D;
+    float s = 0.0f;
+#pragma unroll
+    for (int w2 = 0; w2 < NWAVE; ++w2) s += wsum[((size_t)w2 * GM + g) * D + e];
+    dst[i] = s;
+  }
+}
+
 // PER > 0: the chunk CDF is computed here from the chunk statistics (T <= 64 * PER, the same arithmetic
 // as the chunk CDF kernel, so every block of a head sees the same edges); PER == 0: it is read from the
 // chunk CDF kernel's output. Wave w handles heads w and w + 4 of the group up to the key counts, so a
@@ -203,103 +318,102 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
     for (int L = 0; L < PFL; ++L) warm[hh][L] = *(const uint32_t*)(vbase + jpf[hh] * rstride + L * 128);
   __syncthreads();
 
-  // ---- compact the sampled keys (thread k owns key k)
-  uint32_t mycw[NCW];
-  bool any = false;
-#pragma unroll
-  for (int w = 0; w < NCW; ++w) {
-    mycw[w] = cnt[tid * CW + w];
-    any |= mycw[w] != 0u;
-  }
-  const uint64_t bal = __ballot(any);
-  if (lane == 0) wsum_i[wave] = __popcll(bal);
-  __syncthreads();
-  int before = 0, nu = 0;
-#pragma unroll
-  for (int w = 0; w < NWAVE; ++w) {
-    if (w < wave) before += wsum_i[w];
-    nu += wsum_i[w];
-  }
-  if (any) {
-    const int pos = before + __popcll(bal & ((1ull << lane) - 1ull));
-    lkey[pos] = tid;
-#pragma unroll
-    for (int w = 0; w < NCW; ++w) lcnt[pos][w] = mycw[w];
-  }
-  if (tid == 0) p.unique[(int64_t)grp * T + t] = nu;
-  float* dst = p.partial + ((int64_t)grp * T + t) * G * D;
-  if (nu == 0) {  // block-uniform: nothing sampled here
-    for (int i = tid; i < G * D; i += THREADS) dst[i] = 0.0f;
-    return;
-  }
-  __syncthreads();
-
-  // ---- gather: each listed row once, added with its per-head counts
-  const int rg = tid / LPR, pc = tid % LPR;
-  float acc[GM][EPL];
-#pragma unroll
-  for (int g = 0; g < GM; ++g)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
-  for (int u0 = rg; u0 < nu; u0 += NRG * BATCH) {
-    // list entries past nu re-read the last entry's row and are added with count 0
-    int key[BATCH];
-    uint32_t cw[BATCH][NCW];
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      const int u = u0 + k * NRG;
-      const int uu = min(u, nu - 1);
-      key[k] = lkey[uu];
-#pragma unroll
-      for (int w = 0; w < NCW; ++w) cw[k][w] = u < nu ? lcnt[uu][w] : 0u;
-    }
-    uint4 w4[BATCH];
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) w4[k] = load_stream16((const uint4*)(vbase + key[k] * rstride) + pc);
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      float v[EPL];
-      Pc::to_f32(w4[k], v);
-#pragma unroll
-      for (int g = 0; g < GM; ++g) {
-        const uint32_t c32 = cw[k][g >> 1];
-        const float c = (float)((g & 1) ? (c32 >> 16) : (c32 & 0xFFFFu));
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] += c * v[e];
-      }
-    }
-  }
-  // reduce the row groups: inside the wave by lane permutes, then across waves in LDS
-#pragma unroll
-  for (int g = 0; g < GM; ++g)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float x = acc[g][e];
-#pragma unroll
-      for (int o = LPR; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
-      acc[g][e] = x;
-    }
-  float* wsum = reinterpret_cast<float*>(&Pt[0][0]);  // [NWAVE][GM][D]; Pt is dead after the last sync
-  if (lane < LPR) {
-#pragma unroll
-    for (int g = 0; g < GM; ++g)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) wsum[((size_t)wave * GM + g) * D + pc * EPL + e] = acc[g][e];
-  }
-  __syncthreads();
-  for (int i = tid; i < G * D; i += THREADS) {
-    const int g = i / D, e = i % D;
-    float s = 0.0f;
-#pragma unroll
-    for (int w2 = 0; w2 < NWAVE; ++w2) s += wsum[((size_t)w2 * GM + g) * D + e];
-    dst[i] = s;
-  }
+  chunk_gather<D, BF16, GM>(p, t, kv, b, len, cnt, lkey, lcnt, wsum_i, Pt);
   uint32_t sink = 0u;
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
     for (int L = 0; L < PFL; ++L) sink ^= warm[hh][L];
   if (lane == 0) p.sink[(int64_t)grp * T + t] = sink;  // keeps the cache-warming loads
+}
+
+// S²ANTA-prop, pass 2 (Appendix O, Algorithm 5): the chunk (= tile) of each head has budget S_t from the
+// budget kernel; with x_n = (S_t / l_t) u_n and a0 ~ U(0,1) from Philox counter (t, h, b, 3), key n of the
+// tile is sampled c_n = floor(a0 + P_n) - floor(a0 + P_{n-1}) times, P_n = (S_t / l_t) * (in-chunk
+// prefix of u up to n) (the running sum p of Algorithm 5, taken from the score pass's prefix). Thread n
+// owns key n for every head, so the counts need no atomics; the sampled keys fill idx slots
+// [off_t + floor(a0 + P_{n-1}), off_t + floor(a0 + P_n)) of the head's list.
+template <int D, bool BF16, int GM>
+__global__ __launch_bounds__(THREADS) void resolve_prop_kernel(Problem p) {
+  constexpr int NCW = GM / 2;
+  constexpr int CW = NCW + 1;
+  constexpr int NWAVE = THREADS / 64;
+  constexpr int HPW = (GM + NWAVE - 1) / NWAVE;  // heads per wave for the prefix rows
+  __shared__ double Pt[GM][CHUNK];
+  __shared__ uint32_t cnt[CHUNK * CW];
+  __shared__ int32_t lkey[CHUNK];
+  __shared__ uint32_t lcnt[CHUNK][NCW];
+  __shared__ int wsum_i[NWAVE];
+  __shared__ double hInv[GM], hA0[GM], hF[GM], hZ[GM];
+  __shared__ int hS[GM], hOff[GM];
+
+  const int t = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = p.G, S = p.S, T = p.T;
+  const int h0 = kv * G;
+  const int64_t bh0 = (int64_t)b * p.H + h0;
+  const int64_t n0 = (int64_t)t * CHUNK;
+  const int len = (int)min((int64_t)CHUNK, p.nk - n0);
+
+  // every load at once (heads clamped to G - 1, keys to the chunk's last key)
+  double pv[HPW][4];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int64_t bh = bh0 + min(wave + NWAVE * hh, G - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[hh][i] = p.stash[bh * p.stash_stride + n0 + min(4 * lane + i, len - 1)];
+  }
+  const int64_t bhg = bh0 + min(tid, G - 1);
+  const int Bt = p.budget[bhg * T + t], off = p.boff[bhg * T + t];
+  const double lt = p.csum[bhg * T + t], f = p.cscale[bhg * T + t], Z = p.cdf[bhg * (T + 1) + T];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int g = wave + NWAVE * hh;
+    if (g < GM) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Pt[g][4 * lane + i] = pv[hh][i];
+    }
+  }
+  if (tid < G) {
+    hS[tid] = Bt;
+    hOff[tid] = off;
+    hInv[tid] = Bt > 0 ? (double)Bt / lt : 0.0;
+    hA0[tid] = uniform53(p.seed, (uint32_t)t, (uint32_t)(h0 + tid), (uint32_t)b, TAG_PROP);
+    hF[tid] = f;
+    hZ[tid] = Z;
+  }
+  __syncthreads();
+
+  if (p.prob) {  // debug: probabilities of this chunk's keys from the score pass's exponentials
+    for (int i = tid; i < G * len; i += THREADS) {
+      const int g = i / len, k = i % len;
+      double* pr = p.prob + (bh0 + g) * p.nk + n0 + k;
+      *pr = *pr * hF[g] / hZ[g];
+    }
+  }
+
+  uint32_t w[NCW];
+#pragma unroll
+  for (int i = 0; i < NCW; ++i) w[i] = 0u;
+  if (tid < len) {
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+      if (g >= G || hS[g] == 0) continue;
+      const double inv = hInv[g], a0 = hA0[g];
+      const double ylo = a0 + inv * (tid > 0 ? Pt[g][tid - 1] : 0.0);
+      const double yhi = a0 + inv * Pt[g][tid];
+      const int lo = (int)floor(ylo), hi = (int)floor(yhi);
+      const int c = hi > lo ? hi - lo : 0;
+      int32_t* dst = p.idx + (bh0 + g) * S + hOff[g];
+      for (int i = 0; i < c; ++i)
+        if (lo + i < hS[g]) dst[lo + i] = (int32_t)(n0 + tid);
+      w[g >> 1] += (g & 1) ? ((uint32_t)c << 16) : (uint32_t)c;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NCW; ++i) cnt[tid * CW + i] = w[i];
+  __syncthreads();
+  chunk_gather<D, BF16, GM>(p, t, kv, b, len, cnt, lkey, lcnt, wsum_i, Pt);
 }
 
 // out[b, h] = round((sum over chunks of the partials of head h) / S); fp64 sum in chunk order
@@ -373,7 +487,23 @@ hipError_t launch_resolve_dt(const Problem& p, hipStream_t st) {
 
 }  // namespace
 
+template <int D, bool BF16>
+hipError_t launch_prop_dt(const Problem& p, hipStream_t st) {
+  const dim3 grid(p.T, p.Hkv, p.B);
+  if (p.G <= 2)
+    resolve_prop_kernel<D, BF16, 2><<<grid, THREADS, 0, st>>>(p);
+  else if (p.G <= 4)
+    resolve_prop_kernel<D, BF16, 4><<<grid, THREADS, 0, st>>>(p);
+  else
+    resolve_prop_kernel<D, BF16, 8><<<grid, THREADS, 0, st>>>(p);
+  return hipGetLastError();
+}
+
 hipError_t launch_resolve(const Problem& p, hipStream_t st) {
+  if (p.mode == 3) {
+    if (p.d == 128) return p.bf16 ? launch_prop_dt<128, true>(p, st) : launch_prop_dt<128, false>(p, st);
+    return p.bf16 ? launch_prop_dt<64, true>(p, st) : launch_prop_dt<64, false>(p, st);
+  }
   if (p.d == 128) return p.bf16 ? launch_resolve_dt<128, true>(p, st) : launch_resolve_dt<128, false>(p, st);
   return p.bf16 ? launch_resolve_dt<64, true>(p, st) : launch_resolve_dt<64, false>(p, st);
 }

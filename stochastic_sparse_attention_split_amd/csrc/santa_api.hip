@@ -37,7 +37,7 @@ constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-  size_t stash, cmax, csum, cdf, cscale, lastpos, partial, idx, unique, sink, sync_err, total;
+  size_t stash, cmax, csum, cdf, cscale, lastpos, partial, idx, unique, sink, sync_err, budget, boff, total;
 };
 
 // every region is written by the call before it is read: no initial contents are required
@@ -62,6 +62,8 @@ Layout layout(int64_t B, int64_t nk, int64_t H, int64_t Hkv, int64_t d, int64_t 
   L.unique = take((size_t)(B * Hkv * T) * sizeof(int32_t));
   L.sink = take((size_t)(B * Hkv * T) * sizeof(uint32_t));
   L.sync_err = take((size_t)(B * Hkv * T) * sizeof(int32_t));
+  L.budget = take((size_t)(B * H * T) * sizeof(int32_t));
+  L.boff = take((size_t)(B * H * T) * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -102,7 +104,7 @@ int validate_sampled(const santa_args* a, int64_t* seq, int64_t* bstride) {
   if (st) return st;
   if (a->S < 1) return fail(SANTA_ERR_INVALID_ARG, "S must be >= 1 (got %d)", a->S);
   const int base = a->mode & 0xFF, flags = a->mode & ~0xFF;
-  if (base > SANTA_SYS || base < 0 || (flags & ~SANTA_TERNARY_Q))
+  if (base > SANTA_PROP || base < 0 || (flags & ~SANTA_TERNARY_Q))
     return fail(SANTA_ERR_INVALID_ARG, "mode 0x%x has unknown bits", (unsigned)a->mode);
   if (a->S > 65535) return fail(SANTA_ERR_UNSUPPORTED, "S %d exceeds 65535", a->S);
   return SANTA_OK;
@@ -195,6 +197,8 @@ int santa_decode_ex(const santa_args* a) {
   p.unique = (int32_t*)(ws + L.unique);
   p.sink = (uint32_t*)(ws + L.sink);
   p.sync_err = (int32_t*)(ws + L.sync_err);
+  p.budget = (int32_t*)(ws + L.budget);
+  p.boff = (int32_t*)(ws + L.boff);
   p.prob = a->prob_out;
 
   hipStream_t stream = (hipStream_t)a->stream;
@@ -211,8 +215,10 @@ int santa_decode_ex(const santa_args* a) {
   (void)hipGetLastError();  // start from a clean error state
   if ((e = launch_score(p, stream)) != hipSuccess) return hip_fail(e, "score kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  const bool cdf_kernel = p.T > FUSED_CDF_MAX_T;  // otherwise the sampling kernel builds the chunk CDF
+  const bool prop = p.mode == SANTA_PROP;
+  const bool cdf_kernel = !prop && p.T > FUSED_CDF_MAX_T;  // otherwise the sampling kernel builds the chunk CDF
   if (cdf_kernel && (e = launch_chunk_cdf(p, stream)) != hipSuccess) return hip_fail(e, "chunk CDF kernel launch");
+  if (prop && (e = launch_budget(p, stream)) != hipSuccess) return hip_fail(e, "budget kernel launch");
   if ((e = launch_resolve(p, stream)) != hipSuccess) return hip_fail(e, "resolve kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if ((e = launch_merge(p, stream)) != hipSuccess) return hip_fail(e, "merge kernel launch");
@@ -235,7 +241,7 @@ int santa_decode_ex(const santa_args* a) {
     }
     const int64_t esz = p.bf16 ? 2 : 4;
     santa_stats* s = a->stats_out;
-    s->launches = cdf_kernel ? 4 : 3;
+    s->launches = (cdf_kernel || prop) ? 4 : 3;
     s->bytes_k = (int64_t)a->batch * a->nk * a->kv_heads * a->d * esz;
     s->bytes_v = U * a->d * esz;
     s->bytes_qo = 2 * (int64_t)a->batch * a->heads * a->d * esz;

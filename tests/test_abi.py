@@ -41,6 +41,7 @@ def test_header_constants_match_binding():
     defs = dict(re.findall(r"#define\s+(SANTA_[A-Z0-9_]+)\s+(0x[0-9a-fA-F]+|\d+)", text))
     val = {k: int(v, 0) for k, v in defs.items()}
     assert val["SANTA_IID"] == santa.IID and val["SANTA_STRAT"] == santa.STRAT and val["SANTA_SYS"] == santa.SYS
+    assert val["SANTA_PROP"] == santa.PROP
     assert val["SANTA_TERNARY_Q"] == santa.TERNARY_Q
     assert val["SANTA_BF16"] == santa.BF16 and val["SANTA_F32"] == santa.F32
     assert val["SANTA_OK"] == santa.OK and val["SANTA_ERR_HIP"] == santa.ERR_HIP
@@ -63,7 +64,7 @@ def _args(**kw):
     (dict(S=0), santa.ERR_INVALID_ARG),
     (dict(nk=0), santa.ERR_INVALID_ARG),
     (dict(batch=0), santa.ERR_INVALID_ARG),
-    (dict(mode=3), santa.ERR_INVALID_ARG),
+    (dict(mode=4), santa.ERR_INVALID_ARG),
     (dict(mode=0x200), santa.ERR_INVALID_ARG),
     (dict(d=96), santa.ERR_UNSUPPORTED),
     (dict(dtype=7), santa.ERR_UNSUPPORTED),

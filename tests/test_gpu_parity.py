@@ -125,6 +125,41 @@ def test_workspace_needs_no_initial_contents():
     assert np.array_equal(i1.cpu().numpy(), r.idx)
 
 
+PROP_CASES = [
+    # B, H, Hkv, d, nk, dtype, S, ternary, spikes  (S²ANTA-prop, Appendix O Algorithms 3-5, 256-key tiles)
+    (1, 4, 1, 128, 1000, "bf16", 64, False, 2),
+    (2, 8, 2, 128, 3000, "bf16", 128, False, 4),
+    (1, 7, 1, 64, 2049, "bf16", 33, False, 3),
+    (1, 4, 4, 64, 777, "f32", 16, False, 0),
+    (2, 8, 2, 128, 5000, "bf16", 256, True, 6),
+    (1, 16, 2, 128, 1, "bf16", 8, False, 0),
+    (1, 6, 2, 128, 257, "bf16", 5, False, 1),
+    (1, 4, 1, 64, 300000, "bf16", 512, False, 6),
+]
+
+
+@pytest.mark.parametrize("case", PROP_CASES, ids=[f"B{c[0]}H{c[1]}kv{c[2]}d{c[3]}n{c[4]}{c[5]}S{c[6]}"
+                                                  f"{'T' if c[7] else ''}" for c in PROP_CASES])
+def test_prop_cases(case):
+    B, H, Hkv, d, nk, dtype, S, tern, spikes = case
+    log(f"prop case {case}")
+    q, K, V, _ = workloads.make_inputs(B, H, Hkv, d, nk, dtype=dtype, spikes_per_head=spikes,
+                                       rng_seed=zlib.crc32(repr(case).encode()) & 0xFFFF)
+    for seed in (0, 77):
+        rep, r, out, idx = compare(q, K, V, S, "prop", seed, ternary=tern, dtype=dtype, want_prob=(nk <= 5000),
+                                   label=f"prop {case}")
+        log(f"  seed {seed}: {rep}")
+
+
+def test_prop_workload_2_paper_operating_point():
+    """S²ANTA-prop at S = 128, the accuracy-matching budget the paper reports at 32k tokens (Section 3.2)."""
+    w = workloads.make(2)
+    log(f"prop workload 2 {w.name}: S=128")
+    rep, *_ = compare(w.q, w.K, w.V, 128, "prop", w.seed, dtype=w.dtype, label=f"{w.name} prop S=128")
+    log(f"  {rep}")
+    assert rep["mismatches"] == 0
+
+
 def test_workload_2_full_size():
     w = workloads.make(2)
     log(f"workload 2 {w.name}: B{w.B} H{w.H}/{w.Hkv} d{w.d} nk{w.nk} {w.mode} S{w.S}")
