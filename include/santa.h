@@ -117,10 +117,12 @@ int santa_decode(const void* q, const void* K, const void* V, int64_t nk, int he
 
 /*
  * santa_decode_ex — the full form. Caller-owned workspace (`workspace`, `workspace_bytes`); never
- * allocates device memory. Launches four kernels on `stream`: the split-K score pass, the chunk CDF per
- * KV group, the sampling and gather-add per (chunk, KV group) (each distinct sampled row read once and
- * added with its per-head counts into an fp32 chunk partial), and the merge that adds the chunk partials
- * of each head and scales by 1/S. Calls sharing one workspace must not overlap.
+ * allocates device memory. Launches three or four kernels on `stream`: the split-K score pass; for more
+ * than 128 chunks of 256 keys, the chunk CDF per KV group (SANTA_PROP: the tile budgets per query head),
+ * which the next kernel otherwise builds itself; the sampling and gather-add per (chunk, KV group) (each
+ * distinct sampled row read once and added with its per-head counts into an fp32 chunk partial); and the
+ * merge that adds the chunk partials of each head and scales by 1/S. Calls sharing one workspace must not
+ * overlap.
  */
 int santa_decode_ex(const santa_args* a);
 

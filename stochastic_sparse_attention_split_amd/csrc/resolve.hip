@@ -327,18 +327,140 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
   if (lane == 0) p.sink[(int64_t)grp * T + t] = sink;  // keeps the cache-warming loads
 }
 
-// S²ANTA-prop, pass 2 (Appendix O, Algorithm 5): the chunk (= tile) of each head has budget S_t from the
-// budget kernel; with x_n = (S_t / l_t) u_n and a0 ~ U(0,1) from Philox counter (t, h, b, 3), key n of the
-// tile is sampled c_n = floor(a0 + P_n) - floor(a0 + P_{n-1}) times, P_n = (S_t / l_t) * (in-chunk
-// prefix of u up to n) (the running sum p of Algorithm 5, taken from the score pass's prefix). Thread n
-// owns key n for every head, so the counts need no atomics; the sampled keys fill idx slots
+// S²ANTA-prop budgets of one head, computed by one wave (Appendix O, Algorithm 4; T <= 64 * PER, lane l
+// owns tiles [l*PER, l*PER + PER)): m* = max m_t, W_t = exp(m_t - m*) l_t, Z = sum W_t, q_t = S W_t / Z,
+// S_t = floor(q_t) plus one for the R = S - sum floor(q_t) largest fractional parts (ties to the lower
+// tile). The winners come from a radix select over the 80-bit keys (fraction bits, 0xFFFF - t), one byte
+// per pass, in a 256-bin LDS histogram owned by this wave; it stops once every key left in the chosen
+// bin wins. Returns the values of tile `t`: S_t, its first slot sum_{t' < t} S_t', exp(m_t - m*), and Z.
+struct TileBudget {
+  int st, off;
+  double f, Z;
+};
+
+__device__ inline int prop_key_byte(uint64_t frac_bits, int t, int pass) {
+  return pass < 8 ? (int)((frac_bits >> (56 - 8 * pass)) & 255u)
+                  : (int)(((uint32_t)(0xFFFF - t) >> (8 * (9 - pass))) & 255u);
+}
+
+template <int PER>
+__device__ inline TileBudget tile_budget_wave(const double* m, const double* l, int T, int S, int t, int lane,
+                                              int* hist) {
+  const int t0 = lane * PER;
+  double mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (t0 + j < T) mx = fmax(mx, m[j]);
+  const double ms = readlane_f64(wave_incl_max_dpp(mx), 63);
+  double e[PER], w[PER], run = 0.0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    e[j] = exp(m[j] - ms);
+    w[j] = t0 + j < T ? e[j] * l[j] : 0.0;
+    run += w[j];
+  }
+  const double Z = readlane_f64(wave_incl_scan_dpp(run), 63);
+  int fl[PER];
+  uint64_t key[PER];
+  uint32_t cand = 0u;
+  double flsum = 0.0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const double q = ((double)S * w[j]) / Z;
+    const double f = floor(q);
+    fl[j] = (int)f;
+    key[j] = (uint64_t)__double_as_longlong(q - f);
+    if (t0 + j < T) {
+      flsum += f;
+      cand |= 1u << j;
+    }
+  }
+  int need = S - (int)readlane_f64(wave_incl_scan_dpp(flsum), 63);
+  uint32_t above = 0u;
+  if (need > 0) {
+    for (int pass = 0; pass < 10; ++pass) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (cand >> j & 1u) atomicAdd(&hist[prop_key_byte(key[j], t0 + j, pass)], 1);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      int c[4], loc = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = hist[4 * lane + i];
+        loc += c[i];
+      }
+      const double incl = wave_incl_scan_dpp((double)loc);  // counts <= 64 * PER are exact
+      const int total = (int)readlane_f64(incl, 63);
+      int through = (int)incl - loc, sd = 0, sneed = 0, sbin = 0;
+      bool found = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        through += c[i];
+        const int hi = total - through;  // keys in higher bins
+        if (hi < need && need <= hi + c[i]) {
+          found = true;
+          sd = 4 * lane + i;
+          sneed = need - hi;
+          sbin = c[i];
+        }
+      }
+      const int owner = __builtin_ctzll(__ballot(found));  // exactly one lane finds the bin
+      const int d = __builtin_amdgcn_readlane(sd, owner), bin = __builtin_amdgcn_readlane(sbin, owner);
+      need = __builtin_amdgcn_readlane(sneed, owner);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        if (!(cand >> j & 1u)) continue;
+        const int kb = prop_key_byte(key[j], t0 + j, pass);
+        if (kb > d) above |= 1u << j;
+        if (kb != d) cand &= ~(1u << j);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // histogram reads done before the next clear
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (need == bin) break;  // wave-uniform; holds at the last pass, where every bin has one key
+    }
+    above |= cand;
+  }
+  double stv[PER], offv[PER], acc = 0.0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    stv[j] = (double)(fl[j] + (int)(above >> j & 1u));
+    offv[j] = acc;  // local exclusive prefix
+    acc += t0 + j < T ? stv[j] : 0.0;
+  }
+  const double inc = wave_incl_scan_dpp(acc);  // integer sums are exact in fp64
+  const double before = inc - acc;
+  const int ol = t / PER, oj = t % PER;
+  TileBudget r;
+  r.st = (int)readlane_f64(pick<PER>(stv, oj), ol);
+  r.off = (int)readlane_f64(before + pick<PER>(offv, oj), ol);
+  r.f = readlane_f64(pick<PER>(e, oj), ol);
+  r.Z = Z;
+  return r;
+}
+
+// S²ANTA-prop, pass 2 (Appendix O, Algorithm 5): the chunk (= tile) of each head has budget S_t; with
+// x_n = (S_t / l_t) u_n and a0 ~ U(0,1) from Philox counter (t, h, b, 3), key n of the tile is sampled
+// c_n = floor(a0 + P_n) - floor(a0 + P_{n-1}) times, P_n = (S_t / l_t) * (in-chunk prefix of u up to n)
+// (the running sum p of Algorithm 5, taken from the score pass's prefix). Thread n owns key n for every
+// head, so the counts need no atomics; the sampled keys fill idx slots
 // [off_t + floor(a0 + P_{n-1}), off_t + floor(a0 + P_n)) of the head's list.
-template <int D, bool BF16, int GM>
+// PER > 0: each wave computes the budgets of its heads itself (tile_budget_wave, T <= 64 * PER), so the
+// budget kernel is not launched; PER == 0: the budgets come from the budget kernel.
+template <int D, bool BF16, int GM, int PER>
 __global__ __launch_bounds__(THREADS) void resolve_prop_kernel(Problem p) {
   constexpr int NCW = GM / 2;
   constexpr int CW = NCW + 1;
   constexpr int NWAVE = THREADS / 64;
-  constexpr int HPW = (GM + NWAVE - 1) / NWAVE;  // heads per wave for the prefix rows
+  constexpr int HPW = (GM + NWAVE - 1) / NWAVE;  // heads per wave
+  constexpr int PL = PER > 0 ? PER : 1;
   __shared__ double Pt[GM][CHUNK];
   __shared__ uint32_t cnt[CHUNK * CW];
   __shared__ int32_t lkey[CHUNK];
@@ -346,6 +468,7 @@ __global__ __launch_bounds__(THREADS) void resolve_prop_kernel(Problem p) {
   __shared__ int wsum_i[NWAVE];
   __shared__ double hInv[GM], hA0[GM], hF[GM], hZ[GM];
   __shared__ int hS[GM], hOff[GM];
+  __shared__ int hist[PER > 0 ? NWAVE : 1][256];
 
   const int t = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -355,17 +478,33 @@ __global__ __launch_bounds__(THREADS) void resolve_prop_kernel(Problem p) {
   const int64_t n0 = (int64_t)t * CHUNK;
   const int len = (int)min((int64_t)CHUNK, p.nk - n0);
 
-  // every load at once (heads clamped to G - 1, keys to the chunk's last key)
+  // every load at once (heads clamped to G - 1, keys to the chunk's last key, tiles to T - 1)
   double pv[HPW][4];
+  double cm[HPW][PL], cl[HPW][PL];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     const int64_t bh = bh0 + min(wave + NWAVE * hh, G - 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) pv[hh][i] = p.stash[bh * p.stash_stride + n0 + min(4 * lane + i, len - 1)];
+    if constexpr (PER > 0) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int tt = min(lane * PER + j, T - 1);
+        cm[hh][j] = p.cmax[bh * T + tt];
+        cl[hh][j] = p.csum[bh * T + tt];
+      }
+    }
   }
   const int64_t bhg = bh0 + min(tid, G - 1);
-  const int Bt = p.budget[bhg * T + t], off = p.boff[bhg * T + t];
-  const double lt = p.csum[bhg * T + t], f = p.cscale[bhg * T + t], Z = p.cdf[bhg * (T + 1) + T];
+  const double lt = p.csum[bhg * T + t];
+  int Bt = 0, off = 0;
+  double f = 0.0, Z = 0.0;
+  if constexpr (PER == 0) {
+    Bt = p.budget[bhg * T + t];
+    off = p.boff[bhg * T + t];
+    f = p.cscale[bhg * T + t];
+    Z = p.cdf[bhg * (T + 1) + T];
+  }
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     const int g = wave + NWAVE * hh;
@@ -373,15 +512,29 @@ __global__ __launch_bounds__(THREADS) void resolve_prop_kernel(Problem p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) Pt[g][4 * lane + i] = pv[hh][i];
     }
+    if constexpr (PER > 0) {
+      if (g < G) {
+        const TileBudget r = tile_budget_wave<PER>(cm[hh], cl[hh], T, S, t, lane, hist[wave]);
+        if (lane == 0) {
+          hS[g] = r.st;
+          hOff[g] = r.off;
+          hF[g] = r.f;
+          hZ[g] = r.Z;
+        }
+      }
+    }
   }
   if (tid < G) {
-    hS[tid] = Bt;
-    hOff[tid] = off;
-    hInv[tid] = Bt > 0 ? (double)Bt / lt : 0.0;
+    if constexpr (PER == 0) {
+      hS[tid] = Bt;
+      hOff[tid] = off;
+      hF[tid] = f;
+      hZ[tid] = Z;
+    }
     hA0[tid] = uniform53(p.seed, (uint32_t)t, (uint32_t)(h0 + tid), (uint32_t)b, TAG_PROP);
-    hF[tid] = f;
-    hZ[tid] = Z;
   }
+  __syncthreads();
+  if (tid < G) hInv[tid] = hS[tid] > 0 ? (double)hS[tid] / lt : 0.0;
   __syncthreads();
 
   if (p.prob) {  // debug: probabilities of this chunk's keys from the score pass's exponentials
@@ -487,16 +640,23 @@ hipError_t launch_resolve_dt(const Problem& p, hipStream_t st) {
 
 }  // namespace
 
+template <int D, bool BF16, int GM>
+hipError_t launch_prop_g(const Problem& p, hipStream_t st) {
+  const dim3 grid(p.T, p.Hkv, p.B);
+  if (p.T <= 64)
+    resolve_prop_kernel<D, BF16, GM, 1><<<grid, THREADS, 0, st>>>(p);
+  else if (p.T <= FUSED_CDF_MAX_T)
+    resolve_prop_kernel<D, BF16, GM, 2><<<grid, THREADS, 0, st>>>(p);
+  else
+    resolve_prop_kernel<D, BF16, GM, 0><<<grid, THREADS, 0, st>>>(p);
+  return hipGetLastError();
+}
+
 template <int D, bool BF16>
 hipError_t launch_prop_dt(const Problem& p, hipStream_t st) {
-  const dim3 grid(p.T, p.Hkv, p.B);
-  if (p.G <= 2)
-    resolve_prop_kernel<D, BF16, 2><<<grid, THREADS, 0, st>>>(p);
-  else if (p.G <= 4)
-    resolve_prop_kernel<D, BF16, 4><<<grid, THREADS, 0, st>>>(p);
-  else
-    resolve_prop_kernel<D, BF16, 8><<<grid, THREADS, 0, st>>>(p);
-  return hipGetLastError();
+  if (p.G <= 2) return launch_prop_g<D, BF16, 2>(p, st);
+  if (p.G <= 4) return launch_prop_g<D, BF16, 4>(p, st);
+  return launch_prop_g<D, BF16, 8>(p, st);
 }
 
 hipError_t launch_resolve(const Problem& p, hipStream_t st) {

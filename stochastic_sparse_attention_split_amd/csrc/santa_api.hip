@@ -216,9 +216,11 @@ int santa_decode_ex(const santa_args* a) {
   if ((e = launch_score(p, stream)) != hipSuccess) return hip_fail(e, "score kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   const bool prop = p.mode == SANTA_PROP;
-  const bool cdf_kernel = !prop && p.T > FUSED_CDF_MAX_T;  // otherwise the sampling kernel builds the chunk CDF
-  if (cdf_kernel && (e = launch_chunk_cdf(p, stream)) != hipSuccess) return hip_fail(e, "chunk CDF kernel launch");
-  if (prop && (e = launch_budget(p, stream)) != hipSuccess) return hip_fail(e, "budget kernel launch");
+  // for T <= FUSED_CDF_MAX_T the sampling kernel builds the chunk CDF (or the prop tile budgets) itself
+  const bool cdf_kernel = p.T > FUSED_CDF_MAX_T;
+  if (cdf_kernel && !prop && (e = launch_chunk_cdf(p, stream)) != hipSuccess)
+    return hip_fail(e, "chunk CDF kernel launch");
+  if (cdf_kernel && prop && (e = launch_budget(p, stream)) != hipSuccess) return hip_fail(e, "budget kernel launch");
   if ((e = launch_resolve(p, stream)) != hipSuccess) return hip_fail(e, "resolve kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if ((e = launch_merge(p, stream)) != hipSuccess) return hip_fail(e, "merge kernel launch");
@@ -241,7 +243,7 @@ int santa_decode_ex(const santa_args* a) {
     }
     const int64_t esz = p.bf16 ? 2 : 4;
     santa_stats* s = a->stats_out;
-    s->launches = (cdf_kernel || prop) ? 4 : 3;
+    s->launches = cdf_kernel ? 4 : 3;
     s->bytes_k = (int64_t)a->batch * a->nk * a->kv_heads * a->d * esz;
     s->bytes_v = U * a->d * esz;
     s->bytes_qo = 2 * (int64_t)a->batch * a->heads * a->d * esz;

@@ -135,6 +135,9 @@ PROP_CASES = [
     (1, 16, 2, 128, 1, "bf16", 8, False, 0),
     (1, 6, 2, 128, 257, "bf16", 5, False, 1),
     (1, 4, 1, 64, 300000, "bf16", 512, False, 6),
+    (1, 4, 1, 64, 100000, "bf16", 300, False, 4),
+    (1, 2, 1, 64, 200000, "f32", 1000, False, 4),
+    (1, 2, 1, 64, 1000000, "bf16", 4000, False, 8),
 ]
 
 
@@ -149,6 +152,21 @@ def test_prop_cases(case):
         rep, r, out, idx = compare(q, K, V, S, "prop", seed, ternary=tern, dtype=dtype, want_prob=(nk <= 5000),
                                    label=f"prop {case}")
         log(f"  seed {seed}: {rep}")
+
+
+@pytest.mark.parametrize("nk,S", [(2560, 37), (2560, 3), (2500, 37), (25600, 1037), (256 * 300, 1000)])
+def test_prop_equal_tiles_break_ties_to_the_lower_tile(nk, S):
+    """A zero query makes every score 0, so all full tiles carry the same mass and their fractional
+    parts of q_t tie exactly; the leftover samples must go to the lowest tile indices (Algorithm 4)."""
+    log(f"prop ties nk={nk} S={S}")
+    q, K, V, _ = workloads.make_inputs(1, 4, 2, 64, nk, dtype="bf16", spikes_per_head=0, rng_seed=nk + S)
+    q = torch.zeros_like(q)
+    rep, r, out, idx = compare(q, K, V, S, "prop", 5, dtype="bf16", want_prob=False, label=f"prop ties {nk} {S}")
+    log(f"  {rep}")
+    assert rep["mismatches"] == 0
+    bud = r.extra["budgets"][0, 0]
+    full = bud[: nk // 256]
+    assert full.max() - full.min() <= 1 and np.all(np.diff(full) <= 0)
 
 
 def test_prop_workload_2_paper_operating_point():
