@@ -402,10 +402,11 @@ __device__ inline void wait_vm() {
   else static_assert(N == 0, "unsupported count");
 }
 
-constexpr int SMFMA = 4;                 // matrix-core waves: 64 keys each, one per SIMD
+constexpr int SQUART = 4;                // key quarters of a chunk (64 keys each)
+constexpr int SMFMA = 2 * SQUART;        // matrix-core waves: (key quarter, half of the head dimension)
 constexpr int SSOFT = 4;                 // exponential waves: one head each
 constexpr int SCOPY = 4;                 // copy waves: two per K tile
-constexpr int STHREADS = 64 * (SMFMA + SSOFT + SCOPY);
+constexpr int STHREADS = 64 * (SMFMA + SSOFT + SCOPY);  // 16 waves: four per SIMD
 constexpr int SPIN_LIMIT = 1 << 22;      // bounded waits: a stuck handshake ends the kernel, flagged
 
 template <int D>
@@ -416,6 +417,7 @@ struct SGeo {
   static constexpr int CPW = TILE / 1024 / 2;  // wave-wide 1 KiB copies per copy wave per chunk (32 or 16)
   static constexpr int RPS = 1024 / ROWB;    // rows per 1 KiB copy (4 or 8)
   static constexpr int PP = PPR / 4;         // pieces per lane per row in the matrix-core layout
+  static constexpr int PPH = PP / 2;         // of which one half of the head dimension holds
 };
 
 // byte offset of piece `pc` of row `row` in a tile: pieces are XOR-swizzled by the row, so the 16 rows a
@@ -432,64 +434,57 @@ __device__ inline void signal(int* ctr, int lane) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-// A polling wave drops to the lowest issue priority while it waits (its polls would otherwise take issue
-// slots from the MFMA waves sharing its SIMD) and returns to `prio` once the counter is reached.
-template <int PRIO = 0>
+// A polling wave keeps its issue priority: a poll is a few instructions per sleep, and a waiting wave
+// at the lowest priority is starved by the MFMA waves sharing its SIMD and notices its counter late.
 __device__ inline bool wait_ge(int* ctr, int target) {
   int spins = 0;
-  bool low = false;
   while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
-    if (++spins > SPIN_LIMIT) {
-      if (low) __builtin_amdgcn_s_setprio(PRIO);
-      return false;
-    }
-    if constexpr (PRIO > 0) {
-      if (!low) {
-        __builtin_amdgcn_s_setprio(0);
-        low = true;
-      }
-    }
+    if (++spins > SPIN_LIMIT) return false;
     __builtin_amdgcn_s_sleep(2);
-  }
-  if constexpr (PRIO > 0) {
-    if (low) __builtin_amdgcn_s_setprio(PRIO);
   }
   asm volatile("" ::: "memory");
   return true;
 }
 
-// Streaming score pass for bf16 caches and G <= 4, one block per CU, three roles that meet only through
-// LDS counters (no block-wide barrier after the start), so the K stream, the matrix cores and the
-// exponentials overlap:
-//   * waves 0..3 (one per SIMD): fp64 MFMA over 64 keys each (four 16-key groups; the head dimension
-//     split by element parity gives eight independent accumulation chains) into the score buffer of the
-//     chunk's parity;
-//   * waves 4..7: chunk max, exponentials, in-chunk prefix and the stores of head w - 4;
-//   * waves 8..11: global -> LDS copies (global_load_lds) of the K tiles, waves 8-9 tile 0 with the
-//     block's even chunks, 10-11 tile 1 with the odd ones (wave 10 first copies the queries).
-// Counters (chunk k lives in tile k & 1 and score buffer k & 1; its fill index there is k >> 1):
+// Streaming score pass for bf16 caches and G <= 4, one block of 16 waves per CU, three roles that meet
+// only through LDS counters (no block-wide barrier after the start), so the K stream, the matrix cores
+// and the exponentials overlap:
+//   * waves 0..7 (two per SIMD): fp64 MFMA over key quarter w & 3 (64 keys: four 16-key groups) and
+//     half w >> 2 of the head dimension (element parity gives eight independent accumulation chains per
+//     wave); each writes its partial dot products into the partial row of its half. Two waves per SIMD
+//     keep the fp64 matrix pipe busy where one wave alone leaves it idle between dependent MFMAs, and
+//     neither waits for the other;
+//   * waves 8..11: score = lower + upper partial (a fixed order), then chunk max, exponentials,
+//     in-chunk prefix and the stores of head w - 8;
+//   * waves 12..15: global -> LDS copies (global_load_lds) of the K tiles, waves 12-13 tile 0 with the
+//     block's even chunks, 14-15 tile 1 with the odd ones (wave 14 first copies the queries). The first
+//     chunk of tile 1 is requested only once tile 0 has landed, so across the device the first tiles
+//     arrive before any second one and the matrix cores start half a pass earlier.
+// Counters (chunk k lives in tile k & 1; its fill index there is k >> 1):
 //   ld[j] +1 per copy wave when its half of tile j's current chunk has landed;
-//   use[j] +1 per MFMA wave when its reads of tile j are done;  md +1 per MFMA wave per chunk scored;
-//   sd +1 per exponential wave per chunk finished;  qr queries landed;  pb prologue barrier;
-//   fin waves finished (the last one publishes the block's handshake status).
+//   use[j] +1 per MFMA wave when its reads of tile j are done;  pr +1 per MFMA wave per chunk whose
+//   partials are written;  pc +1 per exponential wave per chunk whose partials it has read;  qr queries
+//   landed;  pb prologue barrier;  fin waves finished (the last one publishes the block's handshake
+//   status).
 template <int D>
 __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   using Sg = SGeo<D>;
-  constexpr int EPL = 8, PP = Sg::PP, CPW = Sg::CPW;
-  constexpr int KPW = CHUNK / SMFMA;  // keys per MFMA wave
+  constexpr int EPL = 8, PPH = Sg::PPH, CPW = Sg::CPW;
+  constexpr int KPW = CHUNK / SQUART;  // keys per MFMA wave
   constexpr int NGR = KPW / 16;       // 16-key groups per MFMA wave
   static_assert(D * 2 * 4 <= 1024, "the queries of a group fit one 1 KiB copy");
 
   __shared__ __align__(16) unsigned char kt[2][Sg::TILE];
-  __shared__ __align__(16) double sc[2][4][CHUNK];
+  __shared__ __align__(16) double part[2][4][CHUNK];  // partial dot products [half of d][head][key]
   __shared__ __align__(16) double qe[4][D + 2];
   __shared__ double hnorm[4];
   __shared__ __align__(16) unsigned char qs[1024];
-  __shared__ int ctr[10];
+  constexpr int NCTR = 10;
+  __shared__ int ctr[NCTR];
   int* ld = &ctr[0];   // [2]
   int* use = &ctr[2];  // [2]
-  int* md = &ctr[4];
-  int* sd = &ctr[5];
+  int* pr = &ctr[4];
+  int* pc = &ctr[5];
   int* qr = &ctr[6];
   int* pb = &ctr[7];
   int* fin = &ctr[8];
@@ -506,7 +501,7 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   const int n = (T - 1 - t0) / step + 1;  // this block's chunks: t0, t0 + step, ...
   int* err = p.sync_err + ((int64_t)b * gridDim.y + kv) * gridDim.x + t0;
 
-  if (tid < 10) ctr[tid] = 0;
+  if (tid < NCTR) ctr[tid] = 0;
   __syncthreads();  // the only block-wide barrier
 
   const int64_t seq_bytes = 2 * p.seq_stride;
@@ -536,7 +531,8 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
       signal(qr, lane);
     }
     for (int k = j, m = 0; k < n && ok; k += 2, ++m) {
-      if (m > 0) ok = wait_ge<3>(&use[j], SMFMA * m);  // the tile's previous chunk is no longer read
+      if (m > 0) ok = wait_ge(&use[j], SMFMA * m);  // the tile's previous chunk is no longer read
+      if (m == 0 && j == 1) ok = wait_ge(&ld[0], 2);  // the block's first chunk goes first
       if (!ok) break;
       const int t = t0 + k * step;
       const int64_t n0 = (int64_t)t * CHUNK;
@@ -607,19 +603,23 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
     const double nrm = p.ternary && act ? hnorm[g] : 1.0;
     const int64_t bh = (int64_t)b * p.H + h0 + (act ? g : 0);
     for (int k = 0; k < n && ok; ++k) {
-      ok = wait_ge<2>(md, SMFMA * (k + 1));  // chunk k's scores are complete
+      ok = wait_ge(pr, SMFMA * (k + 1));  // chunk k's partials are complete
       if (!ok) break;
       if (act) {
         const int t = t0 + k * step;
         const int len = chunk_len(t);
         const int64_t n0 = (int64_t)t * CHUNK;
-        const double* row = &sc[k & 1][g][0];
+        const double2* lo = (const double2*)&part[0][g][4 * lane];
+        const double2* hi = (const double2*)&part[1][g][4 * lane];
+        const double2 l0 = lo[0], l1 = lo[1], h0v = hi[0], h1v = hi[1];
+        signal(pc, lane);  // the partial rows have been read
+        const double raw[4] = {l0.x + h0v.x, l0.y + h0v.y, l1.x + h1v.x, l1.y + h1v.y};
         double sv[4];
         double lmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int kk = 4 * lane + i;
-          double v = row[kk];
+          double v = raw[i];
           if (p.ternary) v = v * nrm;  // (qhat . K) * norm, then * (1/sqrt(dk))
           v = v * p.scale;
           sv[i] = kk < len ? v : -INFINITY;
@@ -636,7 +636,6 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
         const double incl = wave_incl_scan_dpp(run);
         double excl = __shfl_up(incl, 1, 64);
         if (lane == 0) excl = 0.0;
-        signal(sd, lane);  // the score buffer has been read
         // stash rows are CHUNK-padded: the whole chunk is stored, keys past the end repeat the total
         double2* dst = (double2*)(p.stash + bh * p.stash_stride + n0 + 4 * lane);
         dst[0] = make_double2(excl + pre[0], excl + pre[1]);
@@ -652,7 +651,7 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
             if (4 * lane + i < len) pr[4 * lane + i] = ex[i];
         }
       } else {
-        signal(sd, lane);
+        signal(pc, lane);
       }
     }
     finish();
@@ -661,11 +660,12 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
 
   // ---- MFMA waves: 16-key groups x element parity = independent accumulation chains
   const int slot = lane >> 4;
-  double qb[PP][EPL];
+  const int quart = wave & (SQUART - 1), dh = wave / SQUART;  // key quarter, half of the head dimension
+  double qb[PPH][EPL];
 #pragma unroll
-  for (int pp = 0; pp < PP; ++pp)
+  for (int pp = 0; pp < PPH; ++pp)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qb[pp][e] = qe[lane & 3][EPL * (4 * pp + slot) + e];
+    for (int e = 0; e < EPL; ++e) qb[pp][e] = qe[lane & 3][EPL * (4 * (dh * PPH + pp) + slot) + e];
   for (int k = 0; k < n && ok; ++k) {
     ok = wait_ge(&ld[k & 1], 2 * ((k >> 1) + 1));  // chunk k's tile has landed
     if (!ok) break;
@@ -674,11 +674,11 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
 #pragma unroll
     for (int gi = 0; gi < NGR; ++gi) acc[gi][0] = acc[gi][1] = 0.0;
 #pragma unroll
-    for (int pp = 0; pp < PP; ++pp) {
+    for (int pp = 0; pp < PPH; ++pp) {
       uint4 a4[NGR];
 #pragma unroll
       for (int gi = 0; gi < NGR; ++gi)
-        a4[gi] = *(const uint4*)(ks + tile_off<D>(wave * KPW + gi * 16 + (lane & 15), 4 * pp + slot));
+        a4[gi] = *(const uint4*)(ks + tile_off<D>(quart * KPW + gi * 16 + (lane & 15), 4 * (dh * PPH + pp) + slot));
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
 #pragma unroll
@@ -687,14 +687,14 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
                                                                acc[gi][e & 1], 0, 0, 0);
     }
     signal(&use[k & 1], lane);  // this wave's reads of tile k & 1 are complete
-    if (k >= 2) ok = wait_ge(sd, SSOFT * (k - 1));  // score buffer k & 1 was read for chunk k - 2
+    if (k >= 1) ok = wait_ge(pc, SSOFT * k);  // chunk k - 1's partials were read
     if (!ok) break;
 #pragma unroll
     for (int gi = 0; gi < NGR; ++gi) {
-      const int key = wave * KPW + gi * 16 + 4 * ((lane >> 2) & 3) + (lane >> 4);
-      sc[k & 1][lane & 3][key] = acc[gi][0] + acc[gi][1];
+      const int key = quart * KPW + gi * 16 + 4 * ((lane >> 2) & 3) + (lane >> 4);
+      part[dh][lane & 3][key] = acc[gi][0] + acc[gi][1];
     }
-    signal(md, lane);
+    signal(pr, lane);
   }
   finish();
 }
