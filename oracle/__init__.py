@@ -10,5 +10,6 @@ from .santa import (IID, STRAT, SYS, TERNARY_Q, MODE_NAMES, DecodeResult, bytes_
                     scores_ternary, softmax, stratum_weights, ternary_query, var_trace_iid, var_trace_strat)
 from . import philox
 from . import prop
+from . import flash
 
 MODES = {"iid": IID, "strat": STRAT, "sys": SYS}
