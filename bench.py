@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--no-prop", action="store_true", help="skip the S2ANTA-prop (S=128) measurement")
+    ap.add_argument("--no-prop", action="store_true", help="skip the S2ANTA-prop (S=128) and S2ANTA-flash "
+                                                           "(S=2048) measurements")
     ap.add_argument("--profile-steps", action="store_true", help="minimal run for profilers: no CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 64 MiB device copies (scale reference for hardware byte counters)")
@@ -140,6 +141,17 @@ def main():
             prop_step()
         prop_us = timed(prop_step, args.steps, cold=True)
 
+    flash_us = None
+    if not args.no_prop:  # S²ANTA-flash at its 32k operating point (S = 2048), same protocol
+        ws_f = santa.new_workspace(santa.workspace_bytes(w.B, w.nk, w.H, w.Hkv, w.d, 2048, "flash"), dev)
+
+        def flash_step():
+            santa.decode(q, K, V, 2048, "flash", w.seed, ternary=ternary, out=out, workspace=ws_f, stream=stream)
+
+        for _ in range(args.warmup):
+            flash_step()
+        flash_us = timed(flash_step, args.steps, cold=True)
+
     dense_us = None
     if not args.no_dense:
         for _ in range(args.warmup):
@@ -207,6 +219,11 @@ def main():
         res["s2anta_prop_S128"] = {"us_median": round(pmed, 3), "us_mean": round(statistics.fmean(prop_us), 3)}
         if dense_us is not None:
             res["s2anta_prop_S128"]["speedup_vs_dense"] = round(statistics.median(dense_us) / pmed, 3)
+    if flash_us is not None:
+        fmed = statistics.median(flash_us)
+        res["s2anta_flash_S2048"] = {"us_median": round(fmed, 3), "us_mean": round(statistics.fmean(flash_us), 3)}
+        if dense_us is not None:
+            res["s2anta_flash_S2048"]["speedup_vs_dense"] = round(statistics.median(dense_us) / fmed, 3)
 
     if args.copy_calibration:
         src = torch.ones((64 << 20) // 4, dtype=torch.float32, device=dev)

@@ -61,6 +61,13 @@ extern "C" {
                                        x_n = S_t exp(s_n - m_t) / l_t and a0 ~ U(0,1) per (tile, head) from
                                        Philox counter (t, h, b, 3). idx_out lists each head's sampled keys in
                                        increasing order with multiplicity. */
+#define SANTA_FLASH 4               /* S²ANTA-flash (Section 3.3; Appendix P, Algorithms 6-8): every 256-key tile
+                                       gets the same budget S_tile = max(1, round(S / T)) (halves up), its own
+                                       systematic counts with a0 ~ U(0,1) from Philox counter (t, h, b, 4) and
+                                       an fp32 partial sum_n c_n V_n; the merge returns
+                                       (sum_t W_t partial_t) / (Z S_tile), W_t = exp(m_t - m*) l_t. idx_out lists
+                                       T * S_tile keys per head (santa_samples_per_head), tile t's in slots
+                                       [t S_tile, (t+1) S_tile), increasing within a tile. */
 #define SANTA_TERNARY_Q 0x100       /* Bernoulli ternary query for the score stage (Section 5, Eq. 5; B = 1,
                                        norm = max_i |q_i| per (batch, head)) */
 
@@ -89,7 +96,8 @@ typedef struct santa_args {
   int64_t kv_seq_stride;     /* elements between consecutive positions; 0 means kv_heads * d */
   int64_t kv_batch_stride;   /* elements between sequences; 0 means nk * kv_seq_stride */
   int32_t S;                 /* samples per query head, >= 1 */
-  int32_t mode;              /* SANTA_IID | SANTA_STRAT | SANTA_SYS | SANTA_PROP, optionally | SANTA_TERNARY_Q */
+  int32_t mode;              /* SANTA_IID | SANTA_STRAT | SANTA_SYS | SANTA_PROP | SANTA_FLASH, optionally
+                                | SANTA_TERNARY_Q */
   int32_t dtype;             /* SANTA_BF16 or SANTA_F32 */
   int32_t reserved0;
   uint64_t seed;
@@ -99,7 +107,8 @@ typedef struct santa_args {
                                 share it must not overlap */
   size_t workspace_bytes;
   /* optional debug outputs; NULL to skip */
-  int32_t* idx_out;          /* device [batch, heads, S]: sampled key index of each point, in point order */
+  int32_t* idx_out;          /* device [batch, heads, L], L = santa_samples_per_head(nk, S, mode) (= S except
+                                for SANTA_FLASH): sampled key index of each point, in point order */
   double* prob_out;          /* device [batch, heads, nk]: softmax probabilities */
   santa_stats* stats_out;    /* host; the call synchronises the stream to fill it */
   float* stage_ms;           /* host float[4]: GPU time of [score, chunk CDF + resolve, merge, whole call]
@@ -118,16 +127,23 @@ int santa_decode(const void* q, const void* K, const void* V, int64_t nk, int he
 /*
  * santa_decode_ex — the full form. Caller-owned workspace (`workspace`, `workspace_bytes`); never
  * allocates device memory. Launches three or four kernels on `stream`: the split-K score pass; for more
- * than 128 chunks of 256 keys, the chunk CDF per KV group (SANTA_PROP: the tile budgets per query head),
- * which the next kernel otherwise builds itself; the sampling and gather-add per (chunk, KV group) (each
+ * than 128 chunks of 256 keys, the chunk CDF per KV group (SANTA_PROP: the tile budgets per query head;
+ * SANTA_FLASH needs neither), which the next kernel otherwise builds itself; the sampling and gather-add per (chunk, KV group) (each
  * distinct sampled row read once and added with its per-head counts into an fp32 chunk partial); and the
- * merge that adds the chunk partials of each head and scales by 1/S. Calls sharing one workspace must not
- * overlap.
+ * merge that adds the chunk partials of each head and scales by 1/S (SANTA_FLASH: weights each partial by
+ * W_t / (Z S_tile)). Calls sharing one workspace must not overlap.
  */
 int santa_decode_ex(const santa_args* a);
 
 /* Workspace bytes santa_decode_ex needs for these sizes (0 if the sizes are invalid or d is unsupported). */
 size_t santa_workspace_bytes(int batch, int64_t nk, int heads, int kv_heads, int d, int S, int mode);
+
+/*
+ * Number of sampled keys listed per head for these sizes: S for SANTA_IID/STRAT/SYS/PROP, T * S_tile for
+ * SANTA_FLASH (T = ceil(nk / 256), S_tile as defined there). -1 if nk < 1, S < 1 or the mode is unknown.
+ * idx_out must hold batch * heads * this many int32.
+ */
+int64_t santa_samples_per_head(int64_t nk, int S, int mode);
 
 /*
  * santa_dense_decode — dense decode attention softmax(q K^T / sqrt(dk)) V (Section 2, Eq. 1) over the

@@ -26,15 +26,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsanta.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-IID, STRAT, SYS, PROP = 0, 1, 2, 3
+IID, STRAT, SYS, PROP, FLASH = 0, 1, 2, 3, 4
 TERNARY_Q = 0x100
 BF16, F32 = 0, 1
-MODES = {"iid": IID, "strat": STRAT, "sys": SYS, "prop": PROP}
+MODES = {"iid": IID, "strat": STRAT, "sys": SYS, "prop": PROP, "flash": FLASH}
 
 EXPORTED = [
     "santa_decode", "santa_decode_ex", "santa_workspace_bytes", "santa_dense_decode",
     "santa_dense_workspace_bytes", "santa_philox4x32_10", "santa_status_string", "santa_last_error",
-    "santa_version", "santa_release",
+    "santa_version", "santa_release", "santa_samples_per_head",
 ]
 
 
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.santa_decode_ex.argtypes = [ctypes.POINTER(SantaArgs)]
         L.santa_dense_decode.restype = ctypes.c_int
         L.santa_dense_decode.argtypes = [ctypes.POINTER(SantaArgs)]
+        L.santa_samples_per_head.restype = ctypes.c_int64
+        L.santa_samples_per_head.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int]
         L.santa_workspace_bytes.restype = ctypes.c_size_t
         L.santa_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int, ctypes.c_int]
@@ -124,6 +126,11 @@ def _dtype_code(t: torch.Tensor) -> int:
 def _mode_code(mode, ternary: bool) -> int:
     m = MODES[mode] if isinstance(mode, str) else int(mode)
     return m | (TERNARY_Q if ternary else 0)
+
+
+def samples_per_head(nk: int, S: int, mode=STRAT) -> int:
+    """Sampled keys listed per head (the last dimension of idx_out): S, or T * S_tile for "flash"."""
+    return int(lib().santa_samples_per_head(int(nk), int(S), _mode_code(mode, False)))
 
 
 def workspace_bytes(B: int, nk: int, H: int, Hkv: int, d: int, S: int, mode=STRAT) -> int:
@@ -185,8 +192,9 @@ def decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="stra
     a.workspace = workspace.data_ptr()
     a.workspace_bytes = workspace.numel() * workspace.element_size()
     if idx_out is not None:
-        if idx_out.dtype != torch.int32 or idx_out.numel() < a.batch * a.heads * a.S:
-            raise ValueError("idx_out must be int32 with batch*heads*S elements")
+        L = int(lib().santa_samples_per_head(a.nk, a.S, a.mode))
+        if idx_out.dtype != torch.int32 or idx_out.numel() < a.batch * a.heads * L:
+            raise ValueError(f"idx_out must be int32 with batch*heads*{L} elements")
         a.idx_out = idx_out.data_ptr()
     if prob_out is not None:
         if prob_out.dtype != torch.float64 or prob_out.numel() < a.batch * a.heads * a.nk:

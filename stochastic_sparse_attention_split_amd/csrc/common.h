@@ -55,6 +55,7 @@ __host__ __device__ inline double uniform53(uint64_t seed, uint32_t m, uint32_t 
 constexpr uint32_t TAG_POINT = 0;      // i.i.d. / stratified point m
 constexpr uint32_t TAG_SYS = 1;        // systematic offset (m = 0)
 constexpr uint32_t TAG_PROP = 3;       // S²ANTA-prop tile offset a0
+constexpr uint32_t TAG_FLASH = 4;      // S²ANTA-flash tile offset a0
 constexpr uint32_t TAG_BERNOULLI = 2;  // ternary-query element m (+256 n for Bernoulli sample n)
 
 // ---------------------------------------------------------------------------------------------
@@ -235,6 +236,33 @@ __device__ inline void chunk_cdf_wave(const double* m, const double* l, int T, i
   o.last = (int)readlane_f64(wave_incl_max_dpp((double)lp), 63);
 }
 
+// block-wide maximum and sum over NW waves (every thread passes its value; all get the result). The sum
+// is taken in a fixed order: lanes by the DPP scan tree, then the waves in index order. `red` holds NW
+// doubles of LDS; both end with a barrier, so `red` may be reused at once.
+template <int NW>
+__device__ inline double block_max_f64(double v, double* red, int lane, int wave) {
+  v = readlane_f64(wave_incl_max_dpp(v), 63);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double r = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r = fmax(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+template <int NW>
+__device__ inline double block_sum_f64(double v, double* red, int lane, int wave) {
+  v = readlane_f64(wave_incl_scan_dpp(v), 63);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double r = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r += red[w];
+  __syncthreads();
+  return r;
+}
+
 // element j (wave-uniform) of a small register array
 template <int N>
 __device__ inline double pick(const double* a, int j) {
@@ -243,6 +271,13 @@ __device__ inline double pick(const double* a, int j) {
   for (int i = 1; i < N; ++i)
     if (j == i) v = a[i];
   return v;
+}
+
+// S²ANTA-flash uniform tile budget ("Stochastic Sparse Attention for Memory-Bound Inference", Appendix P,
+// Algorithm 6: S_tile ~ S / T, rounded): halves round up, at least one sample per tile
+inline int flash_tile_budget(int S, int64_t T) {
+  const int64_t st = (2 * (int64_t)S + T) / (2 * T);
+  return st < 1 ? 1 : (int)st;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -258,7 +293,9 @@ struct Problem {
   int64_t seq_stride;    // elements
   int64_t batch_stride;  // elements
   int S;
-  int mode;              // 0 iid, 1 strat, 2 sys
+  int mode;              // 0 iid, 1 strat, 2 sys, 3 prop, 4 flash
+  int S_tile;            // S²ANTA-flash: samples per tile
+  int L;                 // sampled keys listed per head (S; T * S_tile for S²ANTA-flash)
   bool ternary;
   bool bf16;
   uint64_t seed;
@@ -274,7 +311,7 @@ struct Problem {
   double* cscale;        // [B, H, T] exp(m_t - m*)
   int32_t* lastpos;      // [B, H] last chunk with W_t > 0
   float* partial;        // [B, Hkv, T, G, d] per-chunk sums of count * V (fp32, exact products)
-  int32_t* idx;          // [B, H, S]
+  int32_t* idx;          // [B, H, L]
   int32_t* unique;       // [B, Hkv, T] distinct sampled keys of each chunk
   uint32_t* sink;        // [B, Hkv, T] values of the cache-warming loads (never read)
   int32_t* sync_err;     // [B, Hkv, T] per score block: 1 if an LDS handshake timed out

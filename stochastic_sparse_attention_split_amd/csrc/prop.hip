@@ -25,29 +25,6 @@ constexpr int BT = 256;
 constexpr int NW = BT / 64;
 constexpr int NPASS = 10;  // 8 bytes of the fraction, 2 bytes of the reversed tile index
 
-__device__ inline double block_max(double v, double* red, int lane, int wave) {
-  v = readlane_f64(wave_incl_max_dpp(v), 63);
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  double r = red[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) r = fmax(r, red[w]);
-  __syncthreads();
-  return r;
-}
-
-// sum in a fixed order: lanes by the DPP scan tree, then waves in index order
-__device__ inline double block_sum(double v, double* red, int lane, int wave) {
-  v = readlane_f64(wave_incl_scan_dpp(v), 63);
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  double r = red[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) r += red[w];
-  __syncthreads();
-  return r;
-}
-
 __device__ inline int key_byte(uint64_t frac_bits, int t, int pass) {
   return pass < 8 ? (int)((frac_bits >> (56 - 8 * pass)) & 255u)
                   : (int)(((uint32_t)(0xFFFF - t) >> (8 * (NPASS - 1 - pass))) & 255u);
@@ -78,7 +55,7 @@ __global__ __launch_bounds__(BT) void budget_kernel(Problem p) {
 #pragma unroll
   for (int k = 0; k < TPT; ++k)
     if (tid + BT * k < T) mx = fmax(mx, m[k]);
-  const double ms = block_max(mx, red, lane, wave);
+  const double ms = block_max_f64<NW>(mx, red, lane, wave);
 
   double w[TPT], part = 0.0;
 #pragma unroll
@@ -88,7 +65,7 @@ __global__ __launch_bounds__(BT) void budget_kernel(Problem p) {
     part += w[k];
     if (tid + BT * k < T) p.cscale[bh * T + tid + BT * k] = e;
   }
-  const double Z = block_sum(part, red, lane, wave);
+  const double Z = block_sum_f64<NW>(part, red, lane, wave);
 
   int fl[TPT];
   uint64_t key[TPT];
@@ -105,7 +82,7 @@ __global__ __launch_bounds__(BT) void budget_kernel(Problem p) {
       cand |= 1u << k;
     }
   }
-  int need = S - (int)block_sum(flsum, red, lane, wave);  // the R leftover samples
+  int need = S - (int)block_sum_f64<NW>(flsum, red, lane, wave);  // the R leftover samples
 
   uint32_t above = 0;  // keys already known to be among the R largest
   if (need > 0) {

@@ -454,8 +454,12 @@ __device__ inline TileBudget tile_budget_wave(const double* m, const double* l, 
 // [off_t + floor(a0 + P_{n-1}), off_t + floor(a0 + P_n)) of the head's list.
 // PER > 0: each wave computes the budgets of its heads itself (tile_budget_wave, T <= 64 * PER), so the
 // budget kernel is not launched; PER == 0: the budgets come from the budget kernel.
+// PER < 0: S²ANTA-flash, kernel 1 ("Stochastic Sparse Attention for Memory-Bound Inference", Section 3.3
+// and Appendix P, Algorithm 7): every tile has the same budget S_tile, its slots are [t S_tile, (t+1)
+// S_tile), a0 comes from Philox counter (t, h, b, 4), and the partials are reweighted by the merge.
 template <int D, bool BF16, int GM, int PER>
 __global__ __launch_bounds__(THREADS) void resolve_prop_kernel(Problem p) {
+  constexpr bool FLASH = PER < 0;
   constexpr int NCW = GM / 2;
   constexpr int CW = NCW + 1;
   constexpr int NWAVE = THREADS / 64;
@@ -499,7 +503,10 @@ __global__ __launch_bounds__(THREADS) void resolve_prop_kernel(Problem p) {
   const double lt = p.csum[bhg * T + t];
   int Bt = 0, off = 0;
   double f = 0.0, Z = 0.0;
-  if constexpr (PER == 0) {
+  if constexpr (FLASH) {
+    Bt = p.S_tile;
+    off = t * p.S_tile;
+  } else if constexpr (PER == 0) {
     Bt = p.budget[bhg * T + t];
     off = p.boff[bhg * T + t];
     f = p.cscale[bhg * T + t];
@@ -525,19 +532,19 @@ __global__ __launch_bounds__(THREADS) void resolve_prop_kernel(Problem p) {
     }
   }
   if (tid < G) {
-    if constexpr (PER == 0) {
+    if constexpr (PER <= 0) {
       hS[tid] = Bt;
       hOff[tid] = off;
       hF[tid] = f;
       hZ[tid] = Z;
     }
-    hA0[tid] = uniform53(p.seed, (uint32_t)t, (uint32_t)(h0 + tid), (uint32_t)b, TAG_PROP);
+    hA0[tid] = uniform53(p.seed, (uint32_t)t, (uint32_t)(h0 + tid), (uint32_t)b, FLASH ? TAG_FLASH : TAG_PROP);
   }
   __syncthreads();
   if (tid < G) hInv[tid] = hS[tid] > 0 ? (double)hS[tid] / lt : 0.0;
   __syncthreads();
 
-  if (p.prob) {  // debug: probabilities of this chunk's keys from the score pass's exponentials
+  if (!FLASH && p.prob) {  // debug: probabilities of this chunk's keys from the score pass's exponentials
     for (int i = tid; i < G * len; i += THREADS) {
       const int g = i / len, k = i % len;
       double* pr = p.prob + (bh0 + g) * p.nk + n0 + k;
@@ -557,7 +564,7 @@ __global__ __launch_bounds__(THREADS) void resolve_prop_kernel(Problem p) {
       const double yhi = a0 + inv * Pt[g][tid];
       const int lo = (int)floor(ylo), hi = (int)floor(yhi);
       const int c = hi > lo ? hi - lo : 0;
-      int32_t* dst = p.idx + (bh0 + g) * S + hOff[g];
+      int32_t* dst = p.idx + (bh0 + g) * p.L + hOff[g];
       for (int i = 0; i < c; ++i)
         if (lo + i < hS[g]) dst[lo + i] = (int32_t)(n0 + tid);
       w[g >> 1] += (g & 1) ? ((uint32_t)c << 16) : (uint32_t)c;
@@ -619,6 +626,84 @@ __global__ __launch_bounds__(THREADS) void merge_kernel(Problem p) {
   }
 }
 
+// S²ANTA-flash, kernel 2 ("Stochastic Sparse Attention for Memory-Bound Inference", Appendix P,
+// Algorithm 8), one block per (query head, sequence): m* = max_t m_t, W_t = exp(m_t - m*) l_t,
+// Z = sum_t W_t, and out = (sum_t W_t Otilde_t) / (Z S_tile) with Otilde_t the fp32 tile partials; the
+// weighted sums run in fp64 in tile order within each of the TS slices, the slices are added in order.
+template <int D, bool BF16>
+__global__ __launch_bounds__(THREADS) void merge_flash_kernel(Problem p) {
+  constexpr int V4 = D / 4;            // float4 pieces per row
+  constexpr int TS = THREADS / V4;     // tile slices
+  constexpr int MB = 16;               // loads in flight per thread
+  constexpr int NW = THREADS / 64;
+  __shared__ double red[TS][D];
+  __shared__ double wt[MAX_CHUNKS];
+  __shared__ double bred[NW];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = p.G, T = p.T;
+  const int kv = h / G, g = h % G;
+  const int64_t bh = (int64_t)b * p.H + h;
+
+  double mx = -INFINITY;
+  for (int t = tid; t < T; t += THREADS) mx = fmax(mx, p.cmax[bh * T + t]);
+  const double ms = block_max_f64<NW>(mx, bred, lane, wave);
+  double part = 0.0;
+  for (int t = tid; t < T; t += THREADS) {
+    const double w = exp(p.cmax[bh * T + t] - ms) * p.csum[bh * T + t];
+    wt[t] = w;
+    part += w;
+  }
+  const double Z = block_sum_f64<NW>(part, bred, lane, wave);  // its barriers also publish wt[]
+
+  const int c = tid % V4, ts = tid / V4;
+  const float* base = p.partial + ((int64_t)(b * p.Hkv + kv) * T * G + g) * D + 4 * c;
+  const int64_t tstride = (int64_t)G * D;
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  for (int t0 = ts; t0 < T; t0 += TS * MB) {
+    float4 v[MB];
+#pragma unroll
+    for (int k = 0; k < MB; ++k) {
+      const int tt = min(t0 + k * TS, T - 1);
+      v[k] = *(const float4*)(base + tt * tstride);
+    }
+#pragma unroll
+    for (int k = 0; k < MB; ++k) {
+      const int tt = t0 + k * TS;
+      if (tt < T) {
+        const double w = wt[tt];
+        a0 += w * (double)v[k].x;
+        a1 += w * (double)v[k].y;
+        a2 += w * (double)v[k].z;
+        a3 += w * (double)v[k].w;
+      }
+    }
+  }
+  red[ts][4 * c + 0] = a0;
+  red[ts][4 * c + 1] = a1;
+  red[ts][4 * c + 2] = a2;
+  red[ts][4 * c + 3] = a3;
+  __syncthreads();
+  if (tid < D) {
+    double tot = 0.0;
+#pragma unroll
+    for (int s = 0; s < TS; ++s) tot += red[s][tid];
+    const double r = tot / (Z * (double)p.S_tile);
+    const int64_t o = bh * D + tid;
+    if (BF16)
+      ((uint16_t*)p.out)[o] = f64_to_bf16_rne(r);
+    else
+      ((float*)p.out)[o] = (float)r;
+  }
+  if (p.prob) {  // debug: probabilities from the score pass's exponentials, exp(s - m_t) exp(m_t - m*) / Z
+    double* pr = p.prob + bh * p.nk;
+    for (int64_t n = tid; n < p.nk; n += THREADS) {
+      const int t = (int)(n / CHUNK);
+      pr[n] = pr[n] * exp(p.cmax[bh * T + t] - ms) / Z;
+    }
+  }
+}
+
 template <int D, bool BF16, int GM>
 hipError_t launch_resolve_g(const Problem& p, hipStream_t st) {
   const dim3 grid(p.T, p.Hkv, p.B);
@@ -643,7 +728,9 @@ hipError_t launch_resolve_dt(const Problem& p, hipStream_t st) {
 template <int D, bool BF16, int GM>
 hipError_t launch_prop_g(const Problem& p, hipStream_t st) {
   const dim3 grid(p.T, p.Hkv, p.B);
-  if (p.T <= 64)
+  if (p.mode == 4)
+    resolve_prop_kernel<D, BF16, GM, -1><<<grid, THREADS, 0, st>>>(p);
+  else if (p.T <= 64)
     resolve_prop_kernel<D, BF16, GM, 1><<<grid, THREADS, 0, st>>>(p);
   else if (p.T <= FUSED_CDF_MAX_T)
     resolve_prop_kernel<D, BF16, GM, 2><<<grid, THREADS, 0, st>>>(p);
@@ -660,7 +747,7 @@ hipError_t launch_prop_dt(const Problem& p, hipStream_t st) {
 }
 
 hipError_t launch_resolve(const Problem& p, hipStream_t st) {
-  if (p.mode == 3) {
+  if (p.mode == 3 || p.mode == 4) {
     if (p.d == 128) return p.bf16 ? launch_prop_dt<128, true>(p, st) : launch_prop_dt<128, false>(p, st);
     return p.bf16 ? launch_prop_dt<64, true>(p, st) : launch_prop_dt<64, false>(p, st);
   }
@@ -670,6 +757,16 @@ hipError_t launch_resolve(const Problem& p, hipStream_t st) {
 
 hipError_t launch_merge(const Problem& p, hipStream_t st) {
   dim3 grid(p.H, p.B);
+  if (p.mode == 4) {
+    if (p.d == 128) {
+      if (p.bf16) merge_flash_kernel<128, true><<<grid, THREADS, 0, st>>>(p);
+      else merge_flash_kernel<128, false><<<grid, THREADS, 0, st>>>(p);
+    } else {
+      if (p.bf16) merge_flash_kernel<64, true><<<grid, THREADS, 0, st>>>(p);
+      else merge_flash_kernel<64, false><<<grid, THREADS, 0, st>>>(p);
+    }
+    return hipGetLastError();
+  }
   if (p.d == 128) {
     if (p.bf16) merge_kernel<128, true><<<grid, THREADS, 0, st>>>(p);
     else merge_kernel<128, false><<<grid, THREADS, 0, st>>>(p);

@@ -41,7 +41,13 @@ struct Layout {
 };
 
 // every region is written by the call before it is read: no initial contents are required
-Layout layout(int64_t B, int64_t nk, int64_t H, int64_t Hkv, int64_t d, int64_t S) {
+// sampled keys listed per head: S, or T * S_tile for S²ANTA-flash
+int64_t list_len(int64_t nk, int S, int mode) {
+  const int64_t T = (nk + CHUNK - 1) / CHUNK;
+  return (mode & 0xFF) == SANTA_FLASH ? T * flash_tile_budget(S, T) : (int64_t)S;
+}
+
+Layout layout(int64_t B, int64_t nk, int64_t H, int64_t Hkv, int64_t d, int64_t S, int mode) {
   const int64_t T = (nk + CHUNK - 1) / CHUNK;
   const int64_t G = H / Hkv;
   Layout L;
@@ -58,7 +64,7 @@ Layout layout(int64_t B, int64_t nk, int64_t H, int64_t Hkv, int64_t d, int64_t 
   L.cscale = take((size_t)(B * H * T) * sizeof(double));
   L.lastpos = take((size_t)(B * H) * sizeof(int32_t));
   L.partial = take((size_t)(B * Hkv * T * G * d) * sizeof(float));
-  L.idx = take((size_t)(B * H * S) * sizeof(int32_t));
+  L.idx = take((size_t)(B * H * list_len(nk, (int)S, mode)) * sizeof(int32_t));
   L.unique = take((size_t)(B * Hkv * T) * sizeof(int32_t));
   L.sink = take((size_t)(B * Hkv * T) * sizeof(uint32_t));
   L.sync_err = take((size_t)(B * Hkv * T) * sizeof(int32_t));
@@ -104,7 +110,7 @@ int validate_sampled(const santa_args* a, int64_t* seq, int64_t* bstride) {
   if (st) return st;
   if (a->S < 1) return fail(SANTA_ERR_INVALID_ARG, "S must be >= 1 (got %d)", a->S);
   const int base = a->mode & 0xFF, flags = a->mode & ~0xFF;
-  if (base > SANTA_PROP || base < 0 || (flags & ~SANTA_TERNARY_Q))
+  if (base > SANTA_FLASH || base < 0 || (flags & ~SANTA_TERNARY_Q))
     return fail(SANTA_ERR_INVALID_ARG, "mode 0x%x has unknown bits", (unsigned)a->mode);
   if (a->S > 65535) return fail(SANTA_ERR_UNSUPPORTED, "S %d exceeds 65535", a->S);
   return SANTA_OK;
@@ -147,10 +153,14 @@ struct Events {
 extern "C" {
 
 size_t santa_workspace_bytes(int batch, int64_t nk, int heads, int kv_heads, int d, int S, int mode) {
-  (void)mode;
   if (batch < 1 || nk < 1 || heads < 1 || kv_heads < 1 || S < 1 || heads % kv_heads) return 0;
   if (d != 64 && d != 128) return 0;
-  return layout(batch, nk, heads, kv_heads, d, S).total;
+  return layout(batch, nk, heads, kv_heads, d, S, mode).total;
+}
+
+int64_t santa_samples_per_head(int64_t nk, int S, int mode) {
+  if (nk < 1 || S < 1 || (mode & 0xFF) < 0 || (mode & 0xFF) > SANTA_FLASH) return -1;
+  return list_len(nk, S, mode);
 }
 
 int santa_decode_ex(const santa_args* a) {
@@ -158,7 +168,7 @@ int santa_decode_ex(const santa_args* a) {
   int64_t seq = 0, bstride = 0;
   int st = validate_sampled(a, &seq, &bstride);
   if (st) return st;
-  const Layout L = layout(a->batch, a->nk, a->heads, a->kv_heads, a->d, a->S);
+  const Layout L = layout(a->batch, a->nk, a->heads, a->kv_heads, a->d, a->S, a->mode);
   if (!a->workspace || a->workspace_bytes < L.total)
     return fail(SANTA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", a->workspace_bytes,
                 L.total);
@@ -184,6 +194,8 @@ int santa_decode_ex(const santa_args* a) {
   p.seed = a->seed;
   p.scale = 1.0 / std::sqrt((double)a->d);
   p.T = (int)((a->nk + CHUNK - 1) / CHUNK);
+  p.S_tile = flash_tile_budget(a->S, p.T);
+  p.L = (int)list_len(a->nk, a->S, a->mode);
   p.score_blocks_per_group = score_blocks_per_group(p.B * p.Hkv, p.T, score_blocks_per_cu(p.d, p.bf16, p.G));
   p.stash = (double*)(ws + L.stash);
   p.stash_stride = (int64_t)p.T * CHUNK;
@@ -216,8 +228,9 @@ int santa_decode_ex(const santa_args* a) {
   if ((e = launch_score(p, stream)) != hipSuccess) return hip_fail(e, "score kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   const bool prop = p.mode == SANTA_PROP;
-  // for T <= FUSED_CDF_MAX_T the sampling kernel builds the chunk CDF (or the prop tile budgets) itself
-  const bool cdf_kernel = p.T > FUSED_CDF_MAX_T;
+  // for T <= FUSED_CDF_MAX_T the sampling kernel builds the chunk CDF (or the prop tile budgets) itself;
+  // S²ANTA-flash needs neither
+  const bool cdf_kernel = p.T > FUSED_CDF_MAX_T && p.mode != SANTA_FLASH;
   if (cdf_kernel && !prop && (e = launch_chunk_cdf(p, stream)) != hipSuccess)
     return hip_fail(e, "chunk CDF kernel launch");
   if (cdf_kernel && prop && (e = launch_budget(p, stream)) != hipSuccess) return hip_fail(e, "budget kernel launch");
@@ -295,7 +308,7 @@ int santa_decode(const void* q, const void* K, const void* V, int64_t nk, int he
   int64_t seq, bs;
   int st = validate_sampled(&a, &seq, &bs);
   if (st) return st;
-  const size_t need = layout(1, nk, heads, kv_heads, d, S).total;
+  const size_t need = layout(1, nk, heads, kv_heads, d, S, mode).total;
   std::lock_guard<std::mutex> lock(g_ws_mu);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);

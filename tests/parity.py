@@ -40,7 +40,7 @@ def run_gpu(q, K, V, S, mode, seed, ternary, dtype, want_prob=True, nk=None):
     qd, Kd, Vd = q.to(dev), K.to(dev), V.to(dev)
     B, H, d = q.shape
     n_keys = K.shape[1] if nk is None else nk
-    idx = torch.empty((B, H, S), dtype=torch.int32, device=dev)
+    idx = torch.empty((B, H, santa.samples_per_head(n_keys, S, mode)), dtype=torch.int32, device=dev)
     prob = torch.empty((B, H, n_keys), dtype=torch.float64, device=dev) if want_prob else None
     out, info = santa.decode(qd, Kd, Vd, S, mode, seed, ternary=ternary, nk=nk, idx_out=idx, prob_out=prob,
                              stats=True)
@@ -61,10 +61,12 @@ def compare(q, K, V, S, mode: str, seed: int, *, ternary=False, dtype="bf16", wa
         r = ref
     elif mode == "prop":
         r = oracle.prop.decode(qn, Kn, Vn, S, seed, out_dtype=dtype, ternary=ternary, keep_prob=want_prob)
+    elif mode == "flash":
+        r = oracle.flash.decode(qn, Kn, Vn, S, seed, out_dtype=dtype, ternary=ternary, keep_prob=want_prob)
     else:
         r = oracle.decode(qn, Kn, Vn, S, oracle.MODES[mode], seed, out_dtype=dtype, ternary=ternary,
                           keep_prob=want_prob)
-    edge = EDGE_PROP if mode == "prop" else EDGE
+    edge = EDGE_PROP if mode in ("prop", "flash") else EDGE
     t2 = time.time()
     rep = {"label": label, "gpu_s": t1 - t0, "oracle_s": t2 - t1}
 
@@ -96,7 +98,10 @@ def compare(q, K, V, S, mode: str, seed: int, *, ternary=False, dtype="bf16", wa
     exact = 0
     for b in range(B):
         for h in range(H):
-            if mism[b, h].any():
+            if mism[b, h].any() and mode == "flash":
+                want = rnd(oracle.flash.estimate_from_idx(np.asarray(Vn[b, :, h // G], dtype=np.float64), ig[b, h],
+                                                          r.extra["weights"][b, h], r.extra["S_tile"]))
+            elif mism[b, h].any():
                 want = rnd(oracle.estimate(np.asarray(Vn[b, :, h // G], dtype=np.float64), ig[b, h], S))
             else:
                 want = r.out[b, h]

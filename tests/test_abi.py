@@ -41,7 +41,7 @@ def test_header_constants_match_binding():
     defs = dict(re.findall(r"#define\s+(SANTA_[A-Z0-9_]+)\s+(0x[0-9a-fA-F]+|\d+)", text))
     val = {k: int(v, 0) for k, v in defs.items()}
     assert val["SANTA_IID"] == santa.IID and val["SANTA_STRAT"] == santa.STRAT and val["SANTA_SYS"] == santa.SYS
-    assert val["SANTA_PROP"] == santa.PROP
+    assert val["SANTA_PROP"] == santa.PROP and val["SANTA_FLASH"] == santa.FLASH
     assert val["SANTA_TERNARY_Q"] == santa.TERNARY_Q
     assert val["SANTA_BF16"] == santa.BF16 and val["SANTA_F32"] == santa.F32
     assert val["SANTA_OK"] == santa.OK and val["SANTA_ERR_HIP"] == santa.ERR_HIP
@@ -64,7 +64,7 @@ def _args(**kw):
     (dict(S=0), santa.ERR_INVALID_ARG),
     (dict(nk=0), santa.ERR_INVALID_ARG),
     (dict(batch=0), santa.ERR_INVALID_ARG),
-    (dict(mode=4), santa.ERR_INVALID_ARG),
+    (dict(mode=5), santa.ERR_INVALID_ARG),
     (dict(mode=0x200), santa.ERR_INVALID_ARG),
     (dict(d=96), santa.ERR_UNSUPPORTED),
     (dict(dtype=7), santa.ERR_UNSUPPORTED),
@@ -109,6 +109,20 @@ def test_workspace_bytes(L):
     assert santa.workspace_bytes(1, 10, 8, 2, 96, S) == 0
     assert santa.dense_workspace_bytes(1, 1024, 8, 2, 128) >= 8 * 2 * 130 * 4
     assert santa.dense_workspace_bytes(1, 1024, 8, 2, 96) == 0
+
+
+def test_samples_per_head(L):
+    from oracle import flash
+    for nk, S in [(1, 1), (256, 7), (1000, 16), (32768, 2048), (32768, 100), (300000, 512), (1 << 20, 65535)]:
+        T = (nk + 255) // 256
+        for m in ("iid", "strat", "sys", "prop"):
+            assert santa.samples_per_head(nk, S, m) == S
+        assert santa.samples_per_head(nk, S, "flash") == T * flash.tile_budget(S, T)
+    assert L.santa_samples_per_head(0, 4, 1) == -1
+    assert L.santa_samples_per_head(10, 0, 1) == -1
+    assert L.santa_samples_per_head(10, 4, 5) == -1
+    # the flash workspace holds the longer index list
+    assert santa.workspace_bytes(1, 32768, 8, 2, 128, 100, "flash") >= santa.workspace_bytes(1, 32768, 8, 2, 128, 100)
 
 
 def test_library_philox_matches_oracle(L):
