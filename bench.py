@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--profile-steps", action="store_true", help="minimal run for profilers: no CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 64 MiB device copies (scale reference for hardware byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark: unique keys and variance trace vs S for every sampling mode "
+                         "(Appendix L/M protocol) on a planted-spike 8k-token single-query input; one JSON line")
+    ap.add_argument("--replicates", type=int, default=256, help="independent seeds per (mode, S) in --sweep")
     return ap.parse_args()
 
 
@@ -65,11 +69,49 @@ def traffic_record(kernel_src: str):
     return rec.get("bytes_per_launch")
 
 
+SWEEP_S = (32, 64, 128, 256, 512, 1024)
+SWEEP_MODES = ("iid", "strat", "sys", "prop", "flash")
+
+
+def run_sweep(args, santa, workloads, torch, np, dev):
+    """Unique keys and variance trace vs S ("Stochastic Sparse Attention for Memory-Bound Inference",
+    Appendix L, Table 17, and Appendix M): per head, U = number of distinct sampled keys and the
+    replicate estimate VarTrace = (1/(R-1)) sum_r ||est_r - mean_r est||^2 over R independent seeds, plus
+    the mean squared error against the dense softmax(qK^T/sqrt(d))V of the same library. fp32 inputs and
+    outputs (bf16 output rounding would blur the variance at large S); the heads' values are averaged."""
+    B, H, Hkv, d, nk = 1, 8, 2, 128, 8192
+    q, K, V, info = workloads.make_inputs(B, H, Hkv, d, nk, dtype="f32", spikes_per_head=32, rng_seed=1017)
+    q, K, V = q.to(dev), K.to(dev), V.to(dev)
+    mu = santa.dense_decode(q, K, V).double()
+    R = max(2, args.replicates)
+    rows = []
+    for mode in SWEEP_MODES:
+        for S in SWEEP_S:
+            L = santa.samples_per_head(nk, S, mode)
+            ws = santa.new_workspace(santa.workspace_bytes(B, nk, H, Hkv, d, S, mode), dev)
+            idx = torch.empty((B, H, L), dtype=torch.int32, device=dev)
+            est = torch.empty((R, B, H, d), dtype=torch.float64, device=dev)
+            uniq = np.zeros((R, H))
+            for r in range(R):
+                o = santa.decode(q, K, V, S, mode, r, workspace=ws, idx_out=idx)
+                est[r] = o.double()
+                ih = idx.cpu().numpy()[0]
+                uniq[r] = [np.unique(ih[h]).size for h in range(H)]
+            m = est.mean(dim=0, keepdim=True)
+            vt = ((est - m) ** 2).sum(dim=3).sum(dim=0) / (R - 1)          # [B, H]
+            mse = ((est - mu.unsqueeze(0)) ** 2).sum(dim=3).mean(dim=0)     # [B, H]
+            rows.append({"mode": mode, "S": S, "samples_per_head": L, "U": round(float(uniq.mean()), 2),
+                         "vartrace": float(vt.mean()), "mse_vs_dense": float(mse.mean())})
+    return {"sweep": "unique keys and variance trace vs S (Appendix L/M protocol)",
+            "workload": f"B{B} H{H}/Hkv{Hkv} d{d} nk{nk} f32, 32 planted keys/head, input seed 1017",
+            "replicates": R, "rows": rows}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding of this "
-              "operator is described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); a multi-GPU sharding of this "
+              "operator is not built.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -83,6 +125,9 @@ def main():
     santa.lib()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    if args.sweep:
+        print(json.dumps(run_sweep(args, santa, workloads, torch, np, dev)), flush=True)
+        return
 
     w = workloads.make(args.config)
     q, K, V = w.q.to(dev), w.K.to(dev), w.V.to(dev)
