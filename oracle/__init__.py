@@ -11,5 +11,6 @@ from .santa import (IID, STRAT, SYS, TERNARY_Q, MODE_NAMES, DecodeResult, bytes_
 from . import philox
 from . import prop
 from . import flash
+from . import group_bernoulli
 
 MODES = {"iid": IID, "strat": STRAT, "sys": SYS}

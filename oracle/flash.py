@@ -82,7 +82,7 @@ def head_estimate(s: np.ndarray, Vmat: np.ndarray, S: int, a0: np.ndarray, tile:
 
 
 def decode(q, K, V, S: int, seed: int, out_dtype: str = "bf16", ternary: bool = False, tile: int = TILE,
-           keep_prob: bool = True) -> DecodeResult:
+           keep_prob: bool = True, scores=None) -> DecodeResult:
     """One decode step of S²ANTA-flash. Same layouts as ``oracle.decode``; ``idx`` has T * S_tile entries
     per head (tile-major, increasing key order with multiplicity inside a tile), ``delta`` the distance of
     the running value a0 + p to the nearest integer at either end of each sampled key."""
@@ -110,7 +110,10 @@ def decode(q, K, V, S: int, seed: int, out_dtype: str = "bf16", ternary: bool = 
             hit = np.zeros(nk, dtype=bool)
             for g in range(G):
                 h = kv * G + g
-                s = scores_ternary(q[b, h], Kf, seed, b, h) if ternary else scores_exact(q[b, h], Kf)
+                if scores is not None:
+                    s = np.asarray(scores[b, h], dtype=np.float64)
+                else:
+                    s = scores_ternary(q[b, h], Kf, seed, b, h) if ternary else scores_exact(q[b, h], Kf)
                 a0 = offsets(seed, b, h, T)
                 e, c, dist, _, W, Z = head_estimate(s, Vf, S, a0, tile)
                 est[b, h] = e

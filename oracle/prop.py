@@ -122,7 +122,7 @@ def head_counts(s: np.ndarray, S: int, seed: int, b: int, h: int, tile: int = TI
 
 
 def decode(q, K, V, S: int, seed: int, out_dtype: str = "bf16", ternary: bool = False, tile: int = TILE,
-           keep_prob: bool = True) -> DecodeResult:
+           keep_prob: bool = True, scores=None) -> DecodeResult:
     """One decode step of S²ANTA-prop. Same layouts as ``oracle.decode``; ``idx`` lists each head's
     sampled keys in increasing order with multiplicity (length S), ``delta`` the distance of the
     running value a0 + p to the nearest integer at either end of each sampled key (a count can only
@@ -148,7 +148,10 @@ def decode(q, K, V, S: int, seed: int, out_dtype: str = "bf16", ternary: bool = 
             hit = np.zeros(nk, dtype=bool)
             for g in range(G):
                 h = kv * G + g
-                s = scores_ternary(q[b, h], Kf, seed, b, h) if ternary else scores_exact(q[b, h], Kf)
+                if scores is not None:
+                    s = np.asarray(scores[b, h], dtype=np.float64)
+                else:
+                    s = scores_ternary(q[b, h], Kf, seed, b, h) if ternary else scores_exact(q[b, h], Kf)
                 c, dist, St = head_counts(s, S, seed, b, h, tile)
                 counts[b, h] = c
                 budget[b, h] = St

@@ -188,7 +188,7 @@ class DecodeResult:
 
 
 def decode(q, K, V, S: int, mode: int, seed: int, out_dtype: str = "bf16", ternary: bool = False,
-           keep_prob: bool = True) -> DecodeResult:
+           keep_prob: bool = True, scores=None) -> DecodeResult:
     """One decode step of SANTA (mode IID) or S²ANTA (STRAT / SYS), with exact or ternary scores.
 
     q: [B, H, d]; K, V: [B, nk, Hkv, d] (sequence-major cache, Appendix Q); any float dtype holding the
@@ -219,7 +219,9 @@ def decode(q, K, V, S: int, mode: int, seed: int, out_dtype: str = "bf16", terna
             group = []
             for g in range(G):
                 h = kv * G + g
-                if ternary:
+                if scores is not None:
+                    s = np.asarray(scores[b, h], dtype=np.float64)
+                elif ternary:
                     s = scores_ternary(q[b, h], Kf, seed, b, h)
                 else:
                     s = scores_exact(q[b, h], Kf)
