@@ -197,6 +197,26 @@ def main():
             flash_step()
         flash_us = timed(flash_step, args.steps, cold=True)
 
+    fm = {}
+    if not args.no_prop:  # feature-major K^T: exact scores and the mean-group-query Bernoulli scores
+        Kt = santa.feature_major(K)
+        info_fm = {}
+
+        def fm_step(gb):
+            return santa.decode(q, Kt, V, w.S, w.mode, w.seed, out=out, workspace=ws, stream=stream,
+                                k_feature_major=True, group_bernoulli=gb)
+
+        for gb in (0, 4, 8):
+            for _ in range(args.warmup):
+                fm_step(gb)
+            us_fm = timed(lambda: fm_step(gb), args.steps, cold=True)
+            _, inf = santa.decode(q, Kt, V, w.S, w.mode, w.seed, out=out, workspace=ws, stats=True,
+                                  k_feature_major=True, group_bernoulli=gb)
+            key = "feature_major_exact" if gb == 0 else f"feature_major_group_bernoulli_B{gb}"
+            fm[key] = {"us_median": round(statistics.median(us_fm), 3),
+                       "k_rows_read_fraction": round(inf["bytes_k"] / info["bytes_k"], 4)}
+        del Kt
+
     dense_us = None
     if not args.no_dense:
         for _ in range(args.warmup):
@@ -264,6 +284,8 @@ def main():
         res["s2anta_prop_S128"] = {"us_median": round(pmed, 3), "us_mean": round(statistics.fmean(prop_us), 3)}
         if dense_us is not None:
             res["s2anta_prop_S128"]["speedup_vs_dense"] = round(statistics.median(dense_us) / pmed, 3)
+    for k_, v_ in fm.items():
+        res[k_] = v_
     if flash_us is not None:
         fmed = statistics.median(flash_us)
         res["s2anta_flash_S2048"] = {"us_median": round(fmed, 3), "us_mean": round(statistics.fmean(flash_us), 3)}

@@ -70,6 +70,17 @@ extern "C" {
                                        [t S_tile, (t+1) S_tile), increasing within a tile. */
 #define SANTA_TERNARY_Q 0x100       /* Bernoulli ternary query for the score stage (Section 5, Eq. 5; B = 1,
                                        norm = max_i |q_i| per (batch, head)) */
+#define SANTA_GROUP_BERNOULLI_Q 0x200 /* mean-group-query Bernoulli scores (Section 5.1, Eq. 6; Appendix C.2,
+                                       Eqs. 10-13): per KV group m_i = mean over its heads of |q_i|,
+                                       norm = max_i m_i, c_i = #{n < B : (n + U_{i,n}) / B < m_i / norm}
+                                       (stratified, U from Philox counter (i, kv, b, 5 + 256 n)), score of head
+                                       g = (sum_i ((norm c_i / B) / m_i) q_{g,i} K_i) / sqrt(dk); features with
+                                       c_i = 0 are not read. Needs SANTA_K_FEATURE_MAJOR and bern_samples = B;
+                                       excludes SANTA_TERNARY_Q */
+#define SANTA_K_FEATURE_MAJOR 0x400 /* K is given feature-major, K^T [batch][kv_heads][d][kt_row_stride]:
+                                       element (b, kv, i, n) at K[b * kt_batch_stride + (kv * d + i) *
+                                       kt_row_stride + n]; V keeps the sequence-major layout. The score pass
+                                       then reads only the feature rows with a non-zero query weight. */
 
 /* element types of q, K, V and out */
 #define SANTA_BF16 0
@@ -77,7 +88,8 @@ extern "C" {
 
 typedef struct santa_stats {
   int32_t launches;      /* kernels launched by the call */
-  int64_t bytes_k;       /* K bytes streamed: batch * nk * kv_heads * d * elt */
+  int64_t bytes_k;       /* K bytes streamed: batch * nk * kv_heads * d * elt (feature-major K: only the
+                            feature rows read, sum over groups of rows * nk * elt) */
   int64_t bytes_v;       /* V bytes gathered: (sum over (b, kv) of distinct sampled rows) * d * elt */
   int64_t bytes_qo;      /* q read + out written: 2 * batch * heads * d * elt */
   int64_t unique_rows;   /* sum over (b, kv) of the distinct sampled rows */
@@ -85,7 +97,8 @@ typedef struct santa_stats {
 
 typedef struct santa_args {
   const void* q;             /* [batch, heads, d] device */
-  const void* K;             /* [batch, nk, kv_heads, d] device (strided, see above) */
+  const void* K;             /* [batch, nk, kv_heads, d] device (strided, see above); with
+                                SANTA_K_FEATURE_MAJOR the K^T layout described there */
   const void* V;             /* same layout as K */
   void* out;                 /* [batch, heads, d] device, same dtype as the inputs */
   int32_t batch;
@@ -97,9 +110,9 @@ typedef struct santa_args {
   int64_t kv_batch_stride;   /* elements between sequences; 0 means nk * kv_seq_stride */
   int32_t S;                 /* samples per query head, >= 1 */
   int32_t mode;              /* SANTA_IID | SANTA_STRAT | SANTA_SYS | SANTA_PROP | SANTA_FLASH, optionally
-                                | SANTA_TERNARY_Q */
+                                | SANTA_TERNARY_Q or SANTA_GROUP_BERNOULLI_Q, | SANTA_K_FEATURE_MAJOR */
   int32_t dtype;             /* SANTA_BF16 or SANTA_F32 */
-  int32_t reserved0;
+  int32_t bern_samples;      /* B of SANTA_GROUP_BERNOULLI_Q, 1..64; ignored otherwise */
   uint64_t seed;
   void* stream;              /* hipStream_t, NULL = default stream */
   void* workspace;           /* device scratch of at least santa_workspace_bytes() bytes; no initial contents
@@ -113,6 +126,10 @@ typedef struct santa_args {
   santa_stats* stats_out;    /* host; the call synchronises the stream to fill it */
   float* stage_ms;           /* host float[4]: GPU time of [score, chunk CDF + resolve, merge, whole call]
                                 from events between the launches; synchronises the stream */
+  /* SANTA_K_FEATURE_MAJOR only (elements); rows must hold at least nk rounded up to 8 and start 16-byte
+     aligned */
+  int64_t kt_row_stride;     /* between feature rows; 0 means nk rounded up to 8 */
+  int64_t kt_batch_stride;   /* between sequences; 0 means kv_heads * d * kt_row_stride */
 } santa_args;
 
 /*

@@ -28,6 +28,8 @@ LIB_PATH = os.path.join(HERE, "libsanta.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 IID, STRAT, SYS, PROP, FLASH = 0, 1, 2, 3, 4
 TERNARY_Q = 0x100
+GROUP_BERNOULLI_Q = 0x200
+K_FEATURE_MAJOR = 0x400
 BF16, F32 = 0, 1
 MODES = {"iid": IID, "strat": STRAT, "sys": SYS, "prop": PROP, "flash": FLASH}
 
@@ -48,10 +50,11 @@ class SantaArgs(ctypes.Structure):
         ("q", ctypes.c_void_p), ("K", ctypes.c_void_p), ("V", ctypes.c_void_p), ("out", ctypes.c_void_p),
         ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("d", ctypes.c_int32),
         ("nk", ctypes.c_int64), ("kv_seq_stride", ctypes.c_int64), ("kv_batch_stride", ctypes.c_int64),
-        ("S", ctypes.c_int32), ("mode", ctypes.c_int32), ("dtype", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("S", ctypes.c_int32), ("mode", ctypes.c_int32), ("dtype", ctypes.c_int32), ("bern_samples", ctypes.c_int32),
         ("seed", ctypes.c_uint64), ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t), ("idx_out", ctypes.c_void_p), ("prob_out", ctypes.c_void_p),
         ("stats_out", ctypes.POINTER(SantaStats)), ("stage_ms", ctypes.POINTER(ctypes.c_float)),
+        ("kt_row_stride", ctypes.c_int64), ("kt_batch_stride", ctypes.c_int64),
     ]
 
 
@@ -147,9 +150,30 @@ def dense_workspace_bytes(B: int, nk: int, H: int, Hkv: int, d: int) -> int:
     return int(lib().santa_dense_workspace_bytes(B, nk, H, Hkv, d))
 
 
-def _fill_common(a: SantaArgs, q, K, V, out, nk, stream):
+def feature_major(K: torch.Tensor) -> torch.Tensor:
+    """K^T [B, Hkv, d, rows] from a sequence-major K [B, nk, Hkv, d]: feature rows of nk keys, padded with
+    zeros to a multiple of 8 keys (the row stride the library needs). Returns a view of the padded tensor
+    narrowed to nk keys; its stride(2) is the padded row stride."""
+    B, nk, Hkv, d = K.shape
+    rows = (nk + 7) // 8 * 8
+    kt = torch.zeros((B, Hkv, d, rows), dtype=K.dtype, device=K.device)
+    kt[..., :nk] = K.permute(0, 2, 3, 1)
+    return kt[..., :nk]
+
+
+def _fill_common(a: SantaArgs, q, K, V, out, nk, stream, k_feature_major: bool = False):
     if q.dim() != 3 or K.dim() != 4 or V.dim() != 4:
-        raise ValueError("q must be [B, H, d]; K and V [B, nk, Hkv, d]")
+        raise ValueError("q must be [B, H, d]; K and V [B, nk, Hkv, d] (K^T [B, Hkv, d, nk] if feature-major)")
+    kptr = K.data_ptr()
+    if k_feature_major:
+        if K.shape != (V.shape[0], V.shape[2], V.shape[3], V.shape[1]) or K.stride(3) != 1 \
+                or K.stride(1) != K.shape[2] * K.stride(2):
+            raise ValueError("feature-major K must be K^T [B, Hkv, d, nk] with unit key stride and packed rows")
+        if K.dtype != V.dtype:
+            raise TypeError("K and V must share one dtype")
+        a.kt_row_stride = K.stride(2)
+        a.kt_batch_stride = K.stride(0)
+        K = V  # the remaining checks and the sequence strides are those of V
     if K.shape != V.shape or K.stride() != V.stride():
         raise ValueError("K and V must have the same shape and strides")
     if not (q.is_contiguous() and out.is_contiguous()):
@@ -159,7 +183,7 @@ def _fill_common(a: SantaArgs, q, K, V, out, nk, stream):
     if not (q.dtype == K.dtype == V.dtype == out.dtype):
         raise TypeError("q, K, V and out must share one dtype")
     B, H, d = q.shape
-    a.q, a.K, a.V, a.out = q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr()
+    a.q, a.K, a.V, a.out = q.data_ptr(), kptr, V.data_ptr(), out.data_ptr()
     a.batch, a.heads, a.kv_heads, a.d = B, H, K.shape[2], d
     a.nk = K.shape[1] if nk is None else int(nk)
     a.kv_seq_stride = K.stride(1)
@@ -173,18 +197,24 @@ def _fill_common(a: SantaArgs, q, K, V, out, nk, stream):
 def decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="strat", seed: int = 0, *,
            ternary: bool = False, nk: int | None = None, out: torch.Tensor | None = None,
            workspace: torch.Tensor | None = None, idx_out: torch.Tensor | None = None,
-           prob_out: torch.Tensor | None = None, stats: bool = False, stage_ms: bool = False, stream=None):
+           prob_out: torch.Tensor | None = None, stats: bool = False, stage_ms: bool = False, stream=None,
+           group_bernoulli: int = 0, k_feature_major: bool = False):
     """One SANTA / S²ANTA decode step through santa_decode_ex.
 
+    k_feature_major: K is K^T [B, Hkv, d, nk] (see feature_major()); group_bernoulli = B > 0 selects the
+    mean-group-query Bernoulli scores with B stratified samples (feature-major K only).
     Returns out, or (out, info) when stats or stage_ms is requested (info holds the stats fields and the
     milliseconds [score, chunk CDF + resolve, merge, total] from events between the launches).
     """
     if out is None:
         out = torch.empty_like(q)
     a = SantaArgs()
-    _fill_common(a, q, K, V, out, nk, stream)
+    _fill_common(a, q, K, V, out, nk, stream, k_feature_major)
     a.S = int(S)
-    a.mode = _mode_code(mode, ternary)
+    a.mode = _mode_code(mode, ternary) | (K_FEATURE_MAJOR if k_feature_major else 0)
+    if group_bernoulli:
+        a.mode |= GROUP_BERNOULLI_Q
+        a.bern_samples = int(group_bernoulli)
     a.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
     need = int(lib().santa_workspace_bytes(a.batch, a.nk, a.heads, a.kv_heads, a.d, a.S, a.mode))
     if workspace is None:

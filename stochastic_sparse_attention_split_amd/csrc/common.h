@@ -56,6 +56,7 @@ constexpr uint32_t TAG_POINT = 0;      // i.i.d. / stratified point m
 constexpr uint32_t TAG_SYS = 1;        // systematic offset (m = 0)
 constexpr uint32_t TAG_PROP = 3;       // S²ANTA-prop tile offset a0
 constexpr uint32_t TAG_FLASH = 4;      // S²ANTA-flash tile offset a0
+constexpr uint32_t TAG_GROUP = 5;      // mean-group Bernoulli feature m (+256 n for sample n)
 constexpr uint32_t TAG_BERNOULLI = 2;  // ternary-query element m (+256 n for Bernoulli sample n)
 
 // ---------------------------------------------------------------------------------------------
@@ -297,6 +298,11 @@ struct Problem {
   int S_tile;            // S²ANTA-flash: samples per tile
   int L;                 // sampled keys listed per head (S; T * S_tile for S²ANTA-flash)
   bool ternary;
+  bool group_bern;       // mean-group-query Bernoulli scores (feature-major K only)
+  int bern;              // Bernoulli samples B of the mean-group query
+  bool kfm;              // K is feature-major: K^T [B][Hkv][d][kt_row_stride]
+  int64_t kt_row_stride;    // elements between feature rows of K^T
+  int64_t kt_batch_stride;  // elements between sequences of K^T
   bool bf16;
   uint64_t seed;
   double scale;          // 1/sqrt(d), formed on the host in fp64
@@ -318,6 +324,7 @@ struct Problem {
   int32_t* budget;       // [B, H, T] S²ANTA-prop tile budgets S_t
   int32_t* boff;         // [B, H, T] exclusive prefix of the budgets (first idx slot of each tile)
   double* prob;          // optional [B, H, nk]
+  int32_t* kfeat;        // [B, Hkv] feature rows of K^T read by the feature-major score pass
 };
 
 }  // namespace santa

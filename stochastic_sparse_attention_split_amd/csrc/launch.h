@@ -8,6 +8,7 @@
 namespace santa {
 
 hipError_t launch_score(const Problem& p, hipStream_t st);     // score.hip
+hipError_t launch_score_fm(const Problem& p, hipStream_t st);  // score_fm.hip: feature-major K^T
 int score_blocks_per_cu(int d, bool bf16, int G);              // resident score blocks per CU (LDS)
 hipError_t launch_chunk_cdf(const Problem& p, hipStream_t st); // score.hip
 hipError_t launch_budget(const Problem& p, hipStream_t st);    // prop.hip: S²ANTA-prop tile budgets

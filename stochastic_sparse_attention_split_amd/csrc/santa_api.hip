@@ -37,7 +37,7 @@ constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-  size_t stash, cmax, csum, cdf, cscale, lastpos, partial, idx, unique, sink, sync_err, budget, boff, total;
+  size_t stash, cmax, csum, cdf, cscale, lastpos, partial, idx, unique, sink, sync_err, budget, boff, kfeat, total;
 };
 
 // every region is written by the call before it is read: no initial contents are required
@@ -70,6 +70,7 @@ Layout layout(int64_t B, int64_t nk, int64_t H, int64_t Hkv, int64_t d, int64_t 
   L.sync_err = take((size_t)(B * Hkv * T) * sizeof(int32_t));
   L.budget = take((size_t)(B * H * T) * sizeof(int32_t));
   L.boff = take((size_t)(B * H * T) * sizeof(int32_t));
+  L.kfeat = take((size_t)(B * Hkv) * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -105,14 +106,40 @@ int validate_common(const santa_args* a, int64_t* seq, int64_t* bstride) {
   return SANTA_OK;
 }
 
-int validate_sampled(const santa_args* a, int64_t* seq, int64_t* bstride) {
+// rows of a feature-major K^T hold at least nk rounded up to 8 elements (4-key vector loads stay inside)
+int64_t kt_row_min(int64_t nk) { return (nk + 7) & ~(int64_t)7; }
+
+int validate_sampled(const santa_args* a, int64_t* seq, int64_t* bstride, int64_t* kt_row, int64_t* kt_batch) {
   int st = validate_common(a, seq, bstride);
   if (st) return st;
   if (a->S < 1) return fail(SANTA_ERR_INVALID_ARG, "S must be >= 1 (got %d)", a->S);
   const int base = a->mode & 0xFF, flags = a->mode & ~0xFF;
-  if (base > SANTA_FLASH || base < 0 || (flags & ~SANTA_TERNARY_Q))
+  if (base > SANTA_FLASH || base < 0 ||
+      (flags & ~(SANTA_TERNARY_Q | SANTA_GROUP_BERNOULLI_Q | SANTA_K_FEATURE_MAJOR)))
     return fail(SANTA_ERR_INVALID_ARG, "mode 0x%x has unknown bits", (unsigned)a->mode);
+  if ((flags & SANTA_TERNARY_Q) && (flags & SANTA_GROUP_BERNOULLI_Q))
+    return fail(SANTA_ERR_INVALID_ARG, "SANTA_TERNARY_Q and SANTA_GROUP_BERNOULLI_Q exclude each other");
+  if ((flags & SANTA_GROUP_BERNOULLI_Q) && !(flags & SANTA_K_FEATURE_MAJOR))
+    return fail(SANTA_ERR_INVALID_ARG, "SANTA_GROUP_BERNOULLI_Q needs SANTA_K_FEATURE_MAJOR");
+  if ((flags & SANTA_GROUP_BERNOULLI_Q) && (a->bern_samples < 1 || a->bern_samples > 64))
+    return fail(SANTA_ERR_INVALID_ARG, "bern_samples %d is not in 1..64", a->bern_samples);
   if (a->S > 65535) return fail(SANTA_ERR_UNSUPPORTED, "S %d exceeds 65535", a->S);
+  *kt_row = 0;
+  *kt_batch = 0;
+  if (flags & SANTA_K_FEATURE_MAJOR) {
+    const int64_t esz = a->dtype == SANTA_BF16 ? 2 : 4;
+    const int64_t r = a->kt_row_stride ? a->kt_row_stride : kt_row_min(a->nk);
+    if (r < kt_row_min(a->nk))
+      return fail(SANTA_ERR_INVALID_ARG, "kt_row_stride %lld < nk rounded up to 8 (%lld)", (long long)r,
+                  (long long)kt_row_min(a->nk));
+    const int64_t bs = a->kt_batch_stride ? a->kt_batch_stride : (int64_t)a->kv_heads * a->d * r;
+    if (a->batch > 1 && bs < (int64_t)a->kv_heads * a->d * r)
+      return fail(SANTA_ERR_INVALID_ARG, "kt_batch_stride %lld < kv_heads*d*kt_row_stride", (long long)bs);
+    if ((r * esz) % 16 || (bs * esz) % 16)
+      return fail(SANTA_ERR_INVALID_ARG, "K^T rows and sequences must start 16-byte aligned");
+    *kt_row = r;
+    *kt_batch = bs;
+  }
   return SANTA_OK;
 }
 
@@ -165,8 +192,8 @@ int64_t santa_samples_per_head(int64_t nk, int S, int mode) {
 
 int santa_decode_ex(const santa_args* a) {
   g_err.clear();
-  int64_t seq = 0, bstride = 0;
-  int st = validate_sampled(a, &seq, &bstride);
+  int64_t seq = 0, bstride = 0, kt_row = 0, kt_batch = 0;
+  int st = validate_sampled(a, &seq, &bstride, &kt_row, &kt_batch);
   if (st) return st;
   const Layout L = layout(a->batch, a->nk, a->heads, a->kv_heads, a->d, a->S, a->mode);
   if (!a->workspace || a->workspace_bytes < L.total)
@@ -190,6 +217,11 @@ int santa_decode_ex(const santa_args* a) {
   p.S = a->S;
   p.mode = a->mode & 0xFF;
   p.ternary = (a->mode & SANTA_TERNARY_Q) != 0;
+  p.group_bern = (a->mode & SANTA_GROUP_BERNOULLI_Q) != 0;
+  p.bern = p.group_bern ? a->bern_samples : 0;
+  p.kfm = (a->mode & SANTA_K_FEATURE_MAJOR) != 0;
+  p.kt_row_stride = kt_row;
+  p.kt_batch_stride = kt_batch;
   p.bf16 = a->dtype == SANTA_BF16;
   p.seed = a->seed;
   p.scale = 1.0 / std::sqrt((double)a->d);
@@ -212,6 +244,7 @@ int santa_decode_ex(const santa_args* a) {
   p.budget = (int32_t*)(ws + L.budget);
   p.boff = (int32_t*)(ws + L.boff);
   p.prob = a->prob_out;
+  p.kfeat = (int32_t*)(ws + L.kfeat);
 
   hipStream_t stream = (hipStream_t)a->stream;
   Events ev;
@@ -225,7 +258,8 @@ int santa_decode_ex(const santa_args* a) {
   hipError_t e;
   if (ev.on && (e = hipEventRecord(ev.e[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   (void)hipGetLastError();  // start from a clean error state
-  if ((e = launch_score(p, stream)) != hipSuccess) return hip_fail(e, "score kernel launch");
+  if ((e = p.kfm ? launch_score_fm(p, stream) : launch_score(p, stream)) != hipSuccess)
+    return hip_fail(e, "score kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   const bool prop = p.mode == SANTA_PROP;
   // for T <= FUSED_CDF_MAX_T the sampling kernel builds the chunk CDF (or the prop tile budgets) itself;
@@ -247,17 +281,25 @@ int santa_decode_ex(const santa_args* a) {
     if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
     int64_t U = 0;
     for (int32_t x : u) U += x;
-    if (p.bf16 && p.G <= 4) {  // the streaming score kernel flags a timed-out LDS handshake per block
+    const int64_t esz = p.bf16 ? 2 : 4;
+    int64_t kbytes = (int64_t)a->batch * a->nk * a->kv_heads * a->d * esz;
+    if (p.kfm) {  // feature rows actually read by the feature-major score pass
+      std::vector<int32_t> kf((size_t)a->batch * a->kv_heads);
+      if ((e = hipMemcpy(kf.data(), p.kfeat, kf.size() * sizeof(int32_t), hipMemcpyDeviceToHost)) != hipSuccess)
+        return hip_fail(e, "hipMemcpy(feature rows)");
+      kbytes = 0;
+      for (int32_t x : kf) kbytes += (int64_t)x * a->nk * esz;
+    }
+    if (!p.kfm && p.bf16 && p.G <= 4) {  // the streaming score kernel flags a timed-out LDS handshake per block
       std::vector<int32_t> fl((size_t)p.score_blocks_per_group * p.Hkv * p.B);
       if ((e = hipMemcpy(fl.data(), p.sync_err, fl.size() * sizeof(int32_t), hipMemcpyDeviceToHost)) != hipSuccess)
         return hip_fail(e, "hipMemcpy(sync flags)");
       for (int32_t x : fl)
         if (x != 0) return fail(SANTA_ERR_HIP, "score kernel: an LDS handshake timed out (%d)", x);
     }
-    const int64_t esz = p.bf16 ? 2 : 4;
     santa_stats* s = a->stats_out;
     s->launches = cdf_kernel ? 4 : 3;
-    s->bytes_k = (int64_t)a->batch * a->nk * a->kv_heads * a->d * esz;
+    s->bytes_k = kbytes;
     s->bytes_v = U * a->d * esz;
     s->bytes_qo = 2 * (int64_t)a->batch * a->heads * a->d * esz;
     s->unique_rows = U;
@@ -305,8 +347,8 @@ int santa_decode(const void* q, const void* K, const void* V, int64_t nk, int he
   a.mode = mode;
   a.dtype = SANTA_BF16;
   a.seed = seed;
-  int64_t seq, bs;
-  int st = validate_sampled(&a, &seq, &bs);
+  int64_t seq, bs, ktr, ktb;
+  int st = validate_sampled(&a, &seq, &bs, &ktr, &ktb);
   if (st) return st;
   const size_t need = layout(1, nk, heads, kv_heads, d, S, mode).total;
   std::lock_guard<std::mutex> lock(g_ws_mu);

@@ -35,37 +35,64 @@ def to_np_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_gpu(q, K, V, S, mode, seed, ternary, dtype, want_prob=True, nk=None):
+def run_gpu(q, K, V, S, mode, seed, ternary, dtype, want_prob=True, nk=None, kfm=False, group_b=0):
     dev = torch.device("cuda:0")
     qd, Kd, Vd = q.to(dev), K.to(dev), V.to(dev)
+    if kfm:
+        Kd = santa.feature_major(Kd)
     B, H, d = q.shape
     n_keys = K.shape[1] if nk is None else nk
     idx = torch.empty((B, H, santa.samples_per_head(n_keys, S, mode)), dtype=torch.int32, device=dev)
     prob = torch.empty((B, H, n_keys), dtype=torch.float64, device=dev) if want_prob else None
     out, info = santa.decode(qd, Kd, Vd, S, mode, seed, ternary=ternary, nk=nk, idx_out=idx, prob_out=prob,
-                             stats=True)
+                             stats=True, k_feature_major=kfm, group_bernoulli=group_b)
     torch.cuda.synchronize()
     return out, idx, prob, info
 
 
+def _feature_rows(qn, Kn, seed, ternary, group_b, group_counts):
+    """Feature rows of K^T the feature-major score pass reads: features with a non-zero weight for some
+    head of the group (mean-group Bernoulli: c_i > 0; ternary: qhat != 0 for some head; exact: q != 0)."""
+    B, H, d = qn.shape
+    Hkv = Kn.shape[2]
+    G = H // Hkv
+    rows = 0
+    for b in range(B):
+        for kv in range(Hkv):
+            if group_b:
+                rows += int((group_counts[b, kv] > 0).sum())
+            elif ternary:
+                hit = np.zeros(d, dtype=bool)
+                for g in range(G):
+                    hit |= oracle.ternary_query(qn[b, kv * G + g], seed, b, kv * G + g)[0] != 0.0
+                rows += int(hit.sum())
+            else:
+                rows += int((np.abs(qn[b, kv * G:(kv + 1) * G]).sum(axis=0) > 0).sum())
+    return rows
+
+
 def compare(q, K, V, S, mode: str, seed: int, *, ternary=False, dtype="bf16", want_prob=True, ref=None,
-            nk=None, label=""):
-    """Run GPU and oracle on the same inputs; assert the parity contract; return a report dict."""
+            nk=None, label="", kfm=False, group_b=0):
+    """Run GPU and oracle on the same inputs; assert the parity contract; return a report dict.
+    kfm: K is handed to the library feature-major; group_b > 0: mean-group-query Bernoulli scores."""
     t0 = time.time()
-    out, idx, prob, info = run_gpu(q, K, V, S, mode, seed, ternary, dtype, want_prob, nk)
+    out, idx, prob, info = run_gpu(q, K, V, S, mode, seed, ternary, dtype, want_prob, nk, kfm, group_b)
     if nk is not None:
         K, V = K[:, :nk], V[:, :nk]
     qn, Kn, Vn = q.float().numpy(), K.float().numpy(), V.float().numpy()
     t1 = time.time()
+    sc, gcounts = (oracle.group_bernoulli.scores(qn, Kn, group_b, seed) if group_b else (None, None))
     if ref is not None:
         r = ref
     elif mode == "prop":
-        r = oracle.prop.decode(qn, Kn, Vn, S, seed, out_dtype=dtype, ternary=ternary, keep_prob=want_prob)
+        r = oracle.prop.decode(qn, Kn, Vn, S, seed, out_dtype=dtype, ternary=ternary, keep_prob=want_prob,
+                               scores=sc)
     elif mode == "flash":
-        r = oracle.flash.decode(qn, Kn, Vn, S, seed, out_dtype=dtype, ternary=ternary, keep_prob=want_prob)
+        r = oracle.flash.decode(qn, Kn, Vn, S, seed, out_dtype=dtype, ternary=ternary, keep_prob=want_prob,
+                                scores=sc)
     else:
         r = oracle.decode(qn, Kn, Vn, S, oracle.MODES[mode], seed, out_dtype=dtype, ternary=ternary,
-                          keep_prob=want_prob)
+                          keep_prob=want_prob, scores=sc)
     edge = EDGE_PROP if mode in ("prop", "flash") else EDGE
     t2 = time.time()
     rep = {"label": label, "gpu_s": t1 - t0, "oracle_s": t2 - t1}
@@ -119,7 +146,12 @@ def compare(q, K, V, S, mode: str, seed: int, *, ternary=False, dtype="bf16", wa
         Ug = int(info["unique_rows"])
         assert Ug == int(r.unique.sum()), f"{label}: unique rows {Ug} != oracle {int(r.unique.sum())}"
     esz = 2 if dtype == "bf16" else 4
-    assert info["bytes_k"] == B * Kn.shape[1] * Kn.shape[2] * d * esz
+    if kfm:
+        rows = _feature_rows(qn, Kn, seed, ternary, group_b, gcounts)
+        rep["k_feature_fraction"] = rows / (B * Kn.shape[2] * d)
+        assert info["bytes_k"] == rows * Kn.shape[1] * esz, f"{label}: K bytes {info['bytes_k']} != {rows} rows"
+    else:
+        assert info["bytes_k"] == B * Kn.shape[1] * Kn.shape[2] * d * esz
     assert info["bytes_v"] == info["unique_rows"] * d * esz
     assert info["launches"] >= 1
     rep["unique_rows"] = int(info["unique_rows"])

@@ -43,6 +43,8 @@ def test_header_constants_match_binding():
     assert val["SANTA_IID"] == santa.IID and val["SANTA_STRAT"] == santa.STRAT and val["SANTA_SYS"] == santa.SYS
     assert val["SANTA_PROP"] == santa.PROP and val["SANTA_FLASH"] == santa.FLASH
     assert val["SANTA_TERNARY_Q"] == santa.TERNARY_Q
+    assert val["SANTA_GROUP_BERNOULLI_Q"] == santa.GROUP_BERNOULLI_Q
+    assert val["SANTA_K_FEATURE_MAJOR"] == santa.K_FEATURE_MAJOR
     assert val["SANTA_BF16"] == santa.BF16 and val["SANTA_F32"] == santa.F32
     assert val["SANTA_OK"] == santa.OK and val["SANTA_ERR_HIP"] == santa.ERR_HIP
 
@@ -65,6 +67,15 @@ def _args(**kw):
     (dict(nk=0), santa.ERR_INVALID_ARG),
     (dict(batch=0), santa.ERR_INVALID_ARG),
     (dict(mode=5), santa.ERR_INVALID_ARG),
+    (dict(mode=santa.STRAT | santa.GROUP_BERNOULLI_Q, bern_samples=4), santa.ERR_INVALID_ARG),  # needs K^T
+    (dict(mode=santa.STRAT | santa.GROUP_BERNOULLI_Q | santa.K_FEATURE_MAJOR | santa.TERNARY_Q, bern_samples=4),
+     santa.ERR_INVALID_ARG),
+    (dict(mode=santa.STRAT | santa.GROUP_BERNOULLI_Q | santa.K_FEATURE_MAJOR, bern_samples=0), santa.ERR_INVALID_ARG),
+    (dict(mode=santa.STRAT | santa.GROUP_BERNOULLI_Q | santa.K_FEATURE_MAJOR, bern_samples=65),
+     santa.ERR_INVALID_ARG),
+    (dict(mode=santa.STRAT | santa.K_FEATURE_MAJOR, kt_row_stride=992), santa.ERR_INVALID_ARG),  # < nk
+    (dict(mode=santa.STRAT | santa.K_FEATURE_MAJOR, kt_row_stride=1012), santa.ERR_INVALID_ARG),  # 2024 B rows
+    (dict(mode=santa.STRAT | santa.K_FEATURE_MAJOR, batch=2, kt_batch_stride=8), santa.ERR_INVALID_ARG),
     (dict(mode=0x200), santa.ERR_INVALID_ARG),
     (dict(d=96), santa.ERR_UNSUPPORTED),
     (dict(dtype=7), santa.ERR_UNSUPPORTED),

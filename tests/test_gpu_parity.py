@@ -209,6 +209,45 @@ def test_flash_workload_2(S):
     assert rep["mismatches"] == 0
 
 
+FM_CASES = [
+    # B, H, Hkv, d, nk, dtype, S, mode, ternary, group B, spikes  (feature-major K^T; Section 5.1, App. C.2)
+    (1, 4, 1, 128, 1000, "bf16", 64, "strat", False, 0, 2),     # exact scores from K^T
+    (1, 4, 4, 64, 777, "f32", 16, "iid", False, 0, 0),          # nk not a multiple of 8 (padded rows)
+    (2, 8, 2, 128, 3000, "bf16", 128, "sys", True, 0, 4),       # per-head ternary query, union of features
+    (1, 8, 2, 128, 2049, "bf16", 100, "strat", False, 1, 3),    # mean-group query, B = 1
+    (2, 8, 2, 128, 5000, "bf16", 256, "strat", False, 4, 6),    # B = 4
+    (1, 7, 1, 64, 3001, "bf16", 64, "iid", False, 8, 3),        # G = 7, B = 8
+    (1, 6, 2, 128, 1, "bf16", 8, "sys", False, 4, 0),           # one key
+    (1, 6, 2, 64, 4100, "f32", 64, "prop", False, 4, 2),        # G = 3, with S²ANTA-prop
+    (1, 8, 2, 128, 2600, "bf16", 300, "flash", False, 2, 2),    # with S²ANTA-flash
+]
+
+
+@pytest.mark.parametrize("case", FM_CASES, ids=[f"B{c[0]}H{c[1]}kv{c[2]}d{c[3]}n{c[4]}{c[5]}{c[7]}S{c[6]}"
+                                                f"{'T' if c[8] else ''}g{c[9]}" for c in FM_CASES])
+def test_feature_major_cases(case):
+    B, H, Hkv, d, nk, dtype, S, mode, tern, gb, spikes = case
+    log(f"feature-major case {case}")
+    q, K, V, _ = workloads.make_inputs(B, H, Hkv, d, nk, dtype=dtype, spikes_per_head=spikes,
+                                       rng_seed=zlib.crc32(repr(case).encode()) & 0xFFFF)
+    for seed in (0, 13):
+        rep, *_ = compare(q, K, V, S, mode, seed, ternary=tern, dtype=dtype, want_prob=(nk <= 5000),
+                          label=f"fm {case}", kfm=True, group_b=gb)
+        log(f"  seed {seed}: {rep}")
+
+
+@pytest.mark.parametrize("gb", [4, 8])
+def test_group_bernoulli_workload_2(gb):
+    """The mean-group-query Bernoulli scores on the 32k Llama-3.1-8B-shaped layer, feature-major K^T: the
+    pages report B = 8 on Llama (Section 5.2); the fraction of K^T rows read is logged."""
+    w = workloads.make(2)
+    log(f"group Bernoulli B={gb} workload 2 {w.name}")
+    rep, *_ = compare(w.q, w.K, w.V, w.S, w.mode, w.seed, dtype=w.dtype, label=f"{w.name} group B={gb}",
+                      kfm=True, group_b=gb)
+    log(f"  {rep}")
+    assert rep["mismatches"] == 0
+
+
 def test_prop_workload_2_paper_operating_point():
     """S²ANTA-prop at S = 128, the accuracy-matching budget the paper reports at 32k tokens (Section 3.2)."""
     w = workloads.make(2)
