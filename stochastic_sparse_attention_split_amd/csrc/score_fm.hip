@@ -1,6 +1,6 @@
 // Score pass over a feature-major key cache K^T [batch][kv_heads][d][row stride] ("Stochastic Sparse
-// Attention for Memory-Bound Inference", Section 5.1 and Appendix C.2): one block per (chunk, KV group,
-// sequence). A feature row holds one head dimension of consecutive keys, so a score estimator that
+// Attention for Memory-Bound Inference", Section 5.1 and Appendix C.2): one block per (KPT / 4 chunks,
+// KV group, sequence). A feature row holds one head dimension of consecutive keys, so a score estimator that
 // needs only some features reads only those rows.
 //
 // Query weights w[g][i] (the score of head g is s_{g,n} = (sum_i w[g][i] K_{n,i}) / sqrt(dk)):
@@ -11,7 +11,8 @@
 //     norm = max_i m_i, stratified Bernoulli counts c_i = #{n < B : (n + U_{i,n}) / B < m_i / norm} with
 //     U_{i,n} from Philox counter (i, kv, b, 5 + 256 n), w[g][i] = ((norm c_i) / B) / m_i * q_{g,i}.
 // Features with w[.][i] = 0 for every head of the group are not read. The block's 256 threads are
-// 64 groups of 4 keys x 4 feature slices; each slice accumulates its features in fp64 (bf16 and fp32
+// 64 groups of KPT consecutive keys (one 16-byte load per feature row for bf16 and KPT = 8) x 4 feature
+// slices, so a block covers KPT / 4 chunks; each slice accumulates its features in fp64 (bf16 and fp32
 // values are exact in fp64), the slices are added in a fixed order. The softmax bookkeeping and the
 // stores (chunk max, sum, in-chunk prefix) are those of the sequence-major score pass.
 //
@@ -27,23 +28,38 @@ namespace {
 
 constexpr int FM_THREADS = 256;
 constexpr int FM_SLICES = FM_THREADS / 64;  // feature slices; each wave is one slice
-constexpr int UNR = 4;                      // features in flight per thread
+constexpr int UNR = 8;                      // feature rows in flight per thread
 
-template <bool BF16>
-__device__ inline void load4(const void* base, int64_t off, double* o) {
-  if constexpr (BF16) {
-    const uint2 w = *(const uint2*)((const uint16_t*)base + off);
-    o[0] = (double)bf16_lo(w.x);
-    o[1] = (double)bf16_hi(w.x);
-    o[2] = (double)bf16_lo(w.y);
-    o[3] = (double)bf16_hi(w.y);
+// KPT consecutive elements of a feature row as raw 32-bit words (non-temporal: each row is read once)
+template <bool BF16, int KPT>
+struct Raw {
+  static constexpr int NW = BF16 ? KPT / 2 : KPT;
+  uint32_t w[NW];
+};
+
+template <bool BF16, int KPT>
+__device__ inline Raw<BF16, KPT> load_raw(const void* base, int64_t off) {
+  Raw<BF16, KPT> r;
+  const uint32_t* src = (const uint32_t*)((const char*)base + off * (BF16 ? 2 : 4));
+  if constexpr (Raw<BF16, KPT>::NW == 4) {
+    const uint4 v = load_stream16(src);
+    r.w[0] = v.x;
+    r.w[1] = v.y;
+    r.w[2] = v.z;
+    r.w[3] = v.w;
   } else {
-    const float4 w = *(const float4*)((const float*)base + off);
-    o[0] = (double)w.x;
-    o[1] = (double)w.y;
-    o[2] = (double)w.z;
-    o[3] = (double)w.w;
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t v = __builtin_nontemporal_load((const u32x2_t*)src);
+    r.w[0] = v.x;
+    r.w[1] = v.y;
   }
+  return r;
+}
+
+template <bool BF16, int KPT>
+__device__ inline double raw_elem(const Raw<BF16, KPT>& r, int k) {
+  if constexpr (BF16) return (double)((k & 1) ? bf16_hi(r.w[k >> 1]) : bf16_lo(r.w[k >> 1]));
+  else return (double)__uint_as_float(r.w[k]);
 }
 
 template <bool BF16>
@@ -52,22 +68,24 @@ __device__ inline double load1(const void* base, int64_t off) {
   else return (double)((const float*)base)[off];
 }
 
-template <int D, bool BF16, int GM>
+template <int D, bool BF16, int GM, int KPT>
 __global__ __launch_bounds__(FM_THREADS) void score_fm_kernel(Problem p) {
+  constexpr int KPB = 64 * KPT;        // keys per block
+  constexpr int CPB = KPB / CHUNK;     // chunks per block
+  static_assert(KPB % CHUNK == 0, "a block covers whole chunks");
   __shared__ double w[GM][D];
   __shared__ double qv[GM][D];
-  __shared__ double red[FM_SLICES][GM][CHUNK];
+  __shared__ double red[FM_SLICES][GM][KPB];
   __shared__ int sel[D];
   __shared__ int wcnt[FM_THREADS / 64];
   __shared__ double hn[GM];
   __shared__ double bred[FM_THREADS / 64];
 
-  const int t = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int tb = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = p.G, T = p.T;
   const int h0 = kv * G;
-  const int64_t n0 = (int64_t)t * CHUNK;
-  const int len = (int)min((int64_t)CHUNK, p.nk - n0);
+  const int64_t nb0 = (int64_t)tb * KPB;  // first key of the block
 
   // ---- query weights of the group (every block recomputes them: d x G values and d x B generator calls)
   for (int i = tid; i < GM * D; i += FM_THREADS) {
@@ -128,25 +146,26 @@ __global__ __launch_bounds__(FM_THREADS) void score_fm_kernel(Problem p) {
   const int before = (wave > 0 ? wcnt[0] : 0) + (wave > 1 ? wcnt[1] : 0) + (wave > 2 ? wcnt[2] : 0);
   if (keep) sel[before + __builtin_popcountll(bal & ((1ull << lane) - 1ull))] = tid;
   const int nsel = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
-  if (t == 0 && tid == 0) p.kfeat[(int64_t)b * p.Hkv + kv] = nsel;
+  if (tb == 0 && tid == 0) p.kfeat[(int64_t)b * p.Hkv + kv] = nsel;
   __syncthreads();
 
-  // ---- feature rows: thread (slice, key group) accumulates 4 keys x GM heads over its features
+  // ---- feature rows: thread (slice, key group) accumulates KPT keys x GM heads over its features
   const int kg = tid & 63, sl = tid >> 6;
-  const int64_t nk4 = (p.nk + 3) & ~(int64_t)3;
-  const int64_t kofs = min(n0 + 4 * kg, nk4 - 4);  // in bounds (rows hold >= nk rounded up to 8); masked below
+  const int64_t nkp = (p.nk + KPT - 1) / KPT * KPT;
+  // in bounds: rows hold >= nk rounded up to 8 >= nkp; groups past the end re-read the last one (masked)
+  const int64_t kofs = min(nb0 + KPT * kg, nkp - KPT);
   const int64_t rbase = (int64_t)b * p.kt_batch_stride + (int64_t)kv * D * p.kt_row_stride + kofs;
-  double acc[GM][4];
+  double acc[GM][KPT];
 #pragma unroll
   for (int g = 0; g < GM; ++g)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc[g][k] = 0.0;
+    for (int k = 0; k < KPT; ++k) acc[g][k] = 0.0;
   for (int j0 = sl; j0 < nsel; j0 += FM_SLICES * UNR) {
-    double x[UNR][4];
+    Raw<BF16, KPT> x[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int j = min(j0 + FM_SLICES * u, nsel - 1);  // valid feature; duplicates are skipped below
-      load4<BF16>(p.K, rbase + (int64_t)sel[j] * p.kt_row_stride, x[u]);
+      x[u] = load_raw<BF16, KPT>(p.K, rbase + (int64_t)sel[j] * p.kt_row_stride);
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
@@ -154,10 +173,10 @@ __global__ __launch_bounds__(FM_THREADS) void score_fm_kernel(Problem p) {
       if (j < nsel) {
         const int f = sel[j];
 #pragma unroll
-        for (int g = 0; g < GM; ++g) {
-          const double wg = w[g][f];
+        for (int k = 0; k < KPT; ++k) {
+          const double xv = raw_elem<BF16, KPT>(x[u], k);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) acc[g][k] = fma(wg, x[u][k], acc[g][k]);
+          for (int g = 0; g < GM; ++g) acc[g][k] = fma(w[g][f], xv, acc[g][k]);
         }
       }
     }
@@ -165,17 +184,23 @@ __global__ __launch_bounds__(FM_THREADS) void score_fm_kernel(Problem p) {
 #pragma unroll
   for (int g = 0; g < GM; ++g)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) red[sl][g][4 * kg + k] = acc[g][k];
+    for (int k = 0; k < KPT; ++k) red[sl][g][KPT * kg + k] = acc[g][k];
   __syncthreads();
 
-  // ---- per head: chunk max, exponentials, in-chunk prefix (a wave per head, 4 keys per lane)
-  for (int g = wave; g < G; g += FM_THREADS / 64) {
+  // ---- per (chunk, head): chunk max, exponentials, in-chunk prefix (a wave per pair, 4 keys per lane)
+  for (int pr = wave; pr < CPB * G; pr += FM_THREADS / 64) {
+    const int c = pr / G, g = pr % G;
+    const int t = tb * CPB + c;
+    if (t >= T) continue;  // wave-uniform
+    const int64_t n0 = (int64_t)t * CHUNK;
+    const int len = (int)min((int64_t)CHUNK, p.nk - n0);
     const int64_t bh = (int64_t)b * p.H + h0 + g;
     double sv[4], lmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int kk = 4 * lane + i;
-      const double raw = ((red[0][g][kk] + red[1][g][kk]) + red[2][g][kk]) + red[3][g][kk];
+      const int rk = c * CHUNK + kk;
+      const double raw = ((red[0][g][rk] + red[1][g][rk]) + red[2][g][rk]) + red[3][g][rk];
       sv[i] = kk < len ? raw * p.scale : -INFINITY;
       lmax = fmax(lmax, sv[i]);
     }
@@ -206,12 +231,20 @@ __global__ __launch_bounds__(FM_THREADS) void score_fm_kernel(Problem p) {
   }
 }
 
+template <int D, bool BF16, int GM, int KPT>
+hipError_t launch_fm(const Problem& p, hipStream_t st) {
+  constexpr int CPB = 64 * KPT / CHUNK;
+  const dim3 grid((p.T + CPB - 1) / CPB, p.Hkv, p.B);
+  score_fm_kernel<D, BF16, GM, KPT><<<grid, FM_THREADS, 0, st>>>(p);
+  return hipGetLastError();
+}
+
 template <int D, bool BF16>
 hipError_t launch_fm_dt(const Problem& p, hipStream_t st) {
-  const dim3 grid(p.T, p.Hkv, p.B);
-  if (p.G <= 4) score_fm_kernel<D, BF16, 4><<<grid, FM_THREADS, 0, st>>>(p);
-  else score_fm_kernel<D, BF16, 8><<<grid, FM_THREADS, 0, st>>>(p);
-  return hipGetLastError();
+  // bf16 with G <= 4: 8 keys per thread (one 16-byte load per feature row); otherwise 4 keys per thread
+  if (p.G > 4) return launch_fm<D, BF16, 8, 4>(p, st);
+  if constexpr (BF16) return launch_fm<D, BF16, 4, 8>(p, st);
+  else return launch_fm<D, BF16, 4, 4>(p, st);
 }
 
 }  // namespace
