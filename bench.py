@@ -13,7 +13,7 @@ protocol of the paper's kernel benchmark (Appendix Q). Reported alongside:
     dominant kernel (the score pass: algorithmic bytes = K + q per launch);
   * the fp64 oracle timed on the host's cores on the same inputs (a baseline, not the target).
 
-Prints one JSON line. --gpus N > 1 is refused: this build runs on one GPU.
+Prints one JSON line. --gpus N > 1 is refused: the benchmark runs on one GPU.
 """
 
 from __future__ import annotations
