@@ -33,7 +33,7 @@ namespace {
 
 constexpr int THREADS = 256;
 static_assert(THREADS == CHUNK, "one thread per key of a chunk in the compaction");
-constexpr int BATCH = 8;   // V rows in flight per lane
+constexpr int BATCH = 2;   // V rows in flight per lane
 
 __device__ inline double point_of(const Problem& p, int m, int h, int b, double u_sys) {
   if (p.mode == 0) return uniform53(p.seed, (uint32_t)m, (uint32_t)h, (uint32_t)b, TAG_POINT);
