@@ -290,7 +290,7 @@ int santa_decode_ex(const santa_args* a) {
       kbytes = 0;
       for (int32_t x : kf) kbytes += (int64_t)x * a->nk * esz;
     }
-    if (!p.kfm && p.bf16 && p.G <= 4) {  // the streaming score kernel flags a timed-out LDS handshake per block
+    if (!p.kfm && p.bf16) {  // the streaming score kernel flags a timed-out LDS handshake per block
       std::vector<int32_t> fl((size_t)p.score_blocks_per_group * p.Hkv * p.B);
       if ((e = hipMemcpy(fl.data(), p.sync_err, fl.size() * sizeof(int32_t), hipMemcpyDeviceToHost)) != hipSuccess)
         return hip_fail(e, "hipMemcpy(sync flags)");

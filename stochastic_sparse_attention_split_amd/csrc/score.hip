@@ -466,19 +466,25 @@ __device__ inline bool wait_ge(int* ctr, int target) {
 //   partials are written;  pc +1 per exponential wave per chunk whose partials it has read;  qr queries
 //   landed;  pb prologue barrier;  fin waves finished (the last one publishes the block's handshake
 //   status).
-template <int D>
+// HG = head groups of four (G <= 4 * HG). HG = 1: the MFMA wave pair of a key quarter splits the head
+// dimension and the exponential wave adds the two partial rows. HG = 2 (G = 5..8): the pair splits the
+// heads instead (heads 0-3 and 4-7, each over the whole head dimension), each wave writes complete scores
+// and each exponential wave handles heads w - 8 and w - 4.
+template <int D, int HG>
 __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   using Sg = SGeo<D>;
   constexpr int EPL = 8, PPH = Sg::PPH, CPW = Sg::CPW;
   constexpr int KPW = CHUNK / SQUART;  // keys per MFMA wave
   constexpr int NGR = KPW / 16;       // 16-key groups per MFMA wave
-  static_assert(D * 2 * 4 <= 1024, "the queries of a group fit one 1 KiB copy");
+  constexpr int HM = 4 * HG;          // heads held
+  constexpr int NPW = HG == 1 ? PPH : 2 * PPH;  // 4-piece steps of a row per MFMA wave
+  static_assert(D * 2 * HM <= 1024 * HG, "the queries of a group fit HG 1 KiB copies");
 
   __shared__ __align__(16) unsigned char kt[2][Sg::TILE];
-  __shared__ __align__(16) double part[2][4][CHUNK];  // partial dot products [half of d][head][key]
-  __shared__ __align__(16) double qe[4][D + 2];
-  __shared__ double hnorm[4];
-  __shared__ __align__(16) unsigned char qs[1024];
+  __shared__ __align__(16) double part[2][4][CHUNK];  // [half of d | head group][head][key]
+  __shared__ __align__(16) double qe[HM][D + 2];
+  __shared__ double hnorm[HM];
+  __shared__ __align__(16) unsigned char qs[1024 * HG];
   constexpr int NCTR = 10;
   __shared__ int ctr[NCTR];
   int* ld = &ctr[0];   // [2]
@@ -526,7 +532,9 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
     const int j = (wave - SMFMA - SSOFT) >> 1, hf = (wave - SMFMA - SSOFT) & 1;
     if (j == 1 && hf == 0) {
       const char* qsrc = (const char*)p.q + ((int64_t)b * p.H + h0) * D * 2;
-      copy_to_lds16(qsrc + min(lane * 16, G * D * 2 - 16), lds_addr(qs));
+#pragma unroll
+      for (int c = 0; c < HG; ++c)  // bytes past the group's queries re-read its last piece (never used)
+        copy_to_lds16(qsrc + min(c * 1024 + lane * 16, G * D * 2 - 16), lds_addr(qs) + c * 1024);
       wait_vm<0>();
       signal(qr, lane);
     }
@@ -563,7 +571,7 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   };
   ok = wait_ge(qr, 1);
   if (ok) {
-    for (int i = tid; i < 4 * D; i += (SMFMA + SSOFT) * 64) {
+    for (int i = tid; i < HM * D; i += (SMFMA + SSOFT) * 64) {
       const int g = i / D, e = i % D;
       double v = 0.0;
       if (g < G) v = (double)__uint_as_float(((uint32_t)((const uint16_t*)qs)[g * D + e]) << 16);
@@ -572,14 +580,14 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   }
   pbar();
   if (p.ternary) {
-    if (ok && tid < 4) {
+    if (ok && tid < HM) {
       double m = 0.0;
       for (int e = 0; e < D; ++e) m = fmax(m, fabs(qe[tid][e]));
       hnorm[tid] = m;
     }
     pbar();
     if (ok) {
-      for (int i = tid; i < 4 * D; i += (SMFMA + SSOFT) * 64) {
+      for (int i = tid; i < HM * D; i += (SMFMA + SSOFT) * 64) {
         const int g = i / D, e = i % D;
         const double v = qe[g][e];
         const double nrm = hnorm[g];
@@ -595,31 +603,48 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   }
 
   if (wave >= SMFMA) {
-    // ---- exponential waves: head g of every chunk, lane owns keys 4*lane .. 4*lane + 3. Issue priority
-    // above the MFMA waves sharing their SIMD, whose instruction stream would otherwise starve them.
+    // ---- exponential waves: heads w - 8 (+ 4) of every chunk, lane owns keys 4*lane .. 4*lane + 3. Issue
+    // priority above the MFMA waves sharing their SIMD, whose instruction stream would otherwise starve them.
     __builtin_amdgcn_s_setprio(2);
-    const int g = wave - SMFMA;
-    const bool act = g < G;  // wave-uniform
-    const double nrm = p.ternary && act ? hnorm[g] : 1.0;
-    const int64_t bh = (int64_t)b * p.H + h0 + (act ? g : 0);
+    const int g0 = wave - SMFMA;
     for (int k = 0; k < n && ok; ++k) {
       ok = wait_ge(pr, SMFMA * (k + 1));  // chunk k's partials are complete
       if (!ok) break;
-      if (act) {
-        const int t = t0 + k * step;
-        const int len = chunk_len(t);
-        const int64_t n0 = (int64_t)t * CHUNK;
-        const double2* lo = (const double2*)&part[0][g][4 * lane];
-        const double2* hi = (const double2*)&part[1][g][4 * lane];
-        const double2 l0 = lo[0], l1 = lo[1], h0v = hi[0], h1v = hi[1];
-        signal(pc, lane);  // the partial rows have been read
-        const double raw[4] = {l0.x + h0v.x, l0.y + h0v.y, l1.x + h1v.x, l1.y + h1v.y};
+      double raw[HG][4];
+#pragma unroll
+      for (int hx = 0; hx < HG; ++hx) {
+        const double2* lo = (const double2*)&part[HG == 1 ? 0 : hx][g0][4 * lane];
+        const double2 l0 = lo[0], l1 = lo[1];
+        if constexpr (HG == 1) {  // lower + upper half of the head dimension
+          const double2* hi = (const double2*)&part[1][g0][4 * lane];
+          const double2 h0v = hi[0], h1v = hi[1];
+          raw[hx][0] = l0.x + h0v.x;
+          raw[hx][1] = l0.y + h0v.y;
+          raw[hx][2] = l1.x + h1v.x;
+          raw[hx][3] = l1.y + h1v.y;
+        } else {
+          raw[hx][0] = l0.x;
+          raw[hx][1] = l0.y;
+          raw[hx][2] = l1.x;
+          raw[hx][3] = l1.y;
+        }
+      }
+      signal(pc, lane);  // the partial rows have been read
+      const int t = t0 + k * step;
+      const int len = chunk_len(t);
+      const int64_t n0 = (int64_t)t * CHUNK;
+#pragma unroll
+      for (int hx = 0; hx < HG; ++hx) {
+        const int g = g0 + 4 * hx;
+        if (g >= G) continue;  // wave-uniform
+        const double nrm = p.ternary ? hnorm[g] : 1.0;
+        const int64_t bh = (int64_t)b * p.H + h0 + g;
         double sv[4];
         double lmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int kk = 4 * lane + i;
-          double v = raw[i];
+          double v = raw[hx][i];
           if (p.ternary) v = v * nrm;  // (qhat . K) * norm, then * (1/sqrt(dk))
           v = v * p.scale;
           sv[i] = kk < len ? v : -INFINITY;
@@ -650,8 +675,6 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
           for (int i = 0; i < 4; ++i)
             if (4 * lane + i < len) pr[4 * lane + i] = ex[i];
         }
-      } else {
-        signal(pc, lane);
       }
     }
     finish();
@@ -660,12 +683,15 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
 
   // ---- MFMA waves: 16-key groups x element parity = independent accumulation chains
   const int slot = lane >> 4;
-  const int quart = wave & (SQUART - 1), dh = wave / SQUART;  // key quarter, half of the head dimension
-  double qb[PPH][EPL];
+  // key quarter; half of the head dimension (HG = 1) or head group (HG = 2)
+  const int quart = wave & (SQUART - 1), dh = wave / SQUART;
+  const int pbase = HG == 1 ? dh * PPH : 0;         // first 4-piece step of this wave's part of a row
+  const int qrow = HG == 1 ? (lane & 3) : 4 * dh + (lane & 3);
+  double qb[NPW][EPL];
 #pragma unroll
-  for (int pp = 0; pp < PPH; ++pp)
+  for (int pp = 0; pp < NPW; ++pp)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qb[pp][e] = qe[lane & 3][EPL * (4 * (dh * PPH + pp) + slot) + e];
+    for (int e = 0; e < EPL; ++e) qb[pp][e] = qe[qrow][EPL * (4 * (pbase + pp) + slot) + e];
   for (int k = 0; k < n && ok; ++k) {
     ok = wait_ge(&ld[k & 1], 2 * ((k >> 1) + 1));  // chunk k's tile has landed
     if (!ok) break;
@@ -674,11 +700,11 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
 #pragma unroll
     for (int gi = 0; gi < NGR; ++gi) acc[gi][0] = acc[gi][1] = 0.0;
 #pragma unroll
-    for (int pp = 0; pp < PPH; ++pp) {
+    for (int pp = 0; pp < NPW; ++pp) {
       uint4 a4[NGR];
 #pragma unroll
       for (int gi = 0; gi < NGR; ++gi)
-        a4[gi] = *(const uint4*)(ks + tile_off<D>(quart * KPW + gi * 16 + (lane & 15), 4 * (dh * PPH + pp) + slot));
+        a4[gi] = *(const uint4*)(ks + tile_off<D>(quart * KPW + gi * 16 + (lane & 15), 4 * (pbase + pp) + slot));
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
 #pragma unroll
@@ -715,10 +741,13 @@ hipError_t launch_q(const Problem& p, hipStream_t st) {
 template <int D, bool BF16>
 hipError_t launch_d(const Problem& p, hipStream_t st) {
   if constexpr (BF16) {
+    const dim3 grid(p.score_blocks_per_group, p.Hkv, p.B);
     if (p.G <= 4) {
-      score_stream_kernel<D><<<dim3(p.score_blocks_per_group, p.Hkv, p.B), STHREADS, 0, st>>>(p);
+      score_stream_kernel<D, 1><<<grid, STHREADS, 0, st>>>(p);
       return hipGetLastError();
     }
+    score_stream_kernel<D, 2><<<grid, STHREADS, 0, st>>>(p);
+    return hipGetLastError();
   }
   return p.G <= 4 ? launch_q<D, BF16, 1>(p, st) : launch_q<D, BF16, 2>(p, st);
 }
@@ -726,7 +755,7 @@ hipError_t launch_d(const Problem& p, hipStream_t st) {
 }  // namespace
 
 int score_blocks_per_cu(int d, bool bf16, int G) {
-  if (bf16 && G <= 4) return 1;  // streaming form: one block per CU (two K tiles fill most of the LDS)
+  if (bf16) return 1;  // streaming form (G <= 8): one block per CU (two K tiles fill most of the LDS)
   const bool q1 = G <= 4;
   if (d == 128) {
     if (bf16) return q1 ? blocks_per_cu<128, true, 1>() : blocks_per_cu<128, true, 2>();
