@@ -325,6 +325,39 @@ def test_one_hot_and_uniform_attention():
     assert np.array_equal(out.float().cpu().numpy()[0, 0], mean)
 
 
+@pytest.mark.parametrize("mode", ["strat", "prop", "flash"])
+def test_maximum_S_on_one_key(mode):
+    """S = 65535 (the largest budget) on a one-hot softmax: every sample hits one key, so its per-head count
+    is 65535, the largest value the 16-bit per-head count holds, and the output is that key's V row."""
+    log(f"S = 65535 one-hot {mode}")
+    dev = torch.device("cuda:0")
+    nk, d, S = 3000, 128, 65535
+    q, K, V, _ = workloads.make_inputs(1, 4, 1, d, nk, dtype="bf16", rng_seed=5)
+    q[0, 1:] = q[0, 0]
+    K = K * 0.01
+    K[0, 2222, 0] = q[0, 0] * 128.0
+    L = santa.samples_per_head(nk, S, mode)
+    idx = torch.empty((1, 4, L), dtype=torch.int32, device=dev)
+    out = santa.decode(q.to(dev), K.to(dev), V.to(dev), S, mode, 3, idx_out=idx)
+    torch.cuda.synchronize()
+    ih = idx.cpu().numpy()
+    if mode == "flash":  # every other tile's budget samples its own (underflowed) keys, weighted by 0
+        assert np.all(ih[0, :, 8 * (L // 12):9 * (L // 12)] == 2222)
+    else:
+        assert np.all(ih == 2222)
+    assert torch.equal(out.cpu()[0], V[0, 2222, 0].unsqueeze(0).expand(4, d))
+
+
+def test_maximum_sequence_length():
+    """nk = 2^20 keys (4096 chunks, the largest the per-chunk tables hold): strat and prop against the oracle."""
+    nk = 1 << 20
+    q, K, V, _ = workloads.make_inputs(1, 2, 1, 64, nk, dtype="bf16", spikes_per_head=16, rng_seed=77)
+    for mode in ("strat", "prop"):
+        log(f"nk = 2^20 {mode}")
+        rep, *_ = compare(q, K, V, 4096, mode, 21, dtype="bf16", want_prob=False, label=f"nk=2^20 {mode}")
+        log(f"  {rep}")
+
+
 def test_strat_equals_iid_at_S1_and_determinism():
     log("S=1 consistency and determinism")
     dev = torch.device("cuda:0")
