@@ -325,6 +325,8 @@ struct Problem {
   int32_t* boff;         // [B, H, T] exclusive prefix of the budgets (first idx slot of each tile)
   double* prob;          // optional [B, H, nk]
   int32_t* kfeat;        // [B, Hkv] feature rows of K^T read by the feature-major score pass
+  bool fused;            // S²ANTA-flash sampled and gathered inside the streaming score pass
+  uint64_t* bmap;        // [B, Hkv, T, 4, 4] fused S²ANTA-flash: sampled keys of each (chunk, head) as bits
 };
 
 }  // namespace santa

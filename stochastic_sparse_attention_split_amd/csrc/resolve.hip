@@ -695,6 +695,20 @@ __global__ __launch_bounds__(THREADS) void merge_flash_kernel(Problem p) {
     else
       ((float*)p.out)[o] = (float)r;
   }
+  if (p.fused && g == 0) {  // the group's distinct sampled keys per chunk: union of its heads' key bits
+    const int grp = b * p.Hkv + kv;
+    for (int t = tid; t < T; t += THREADS) {
+      const uint64_t* bm = p.bmap + ((int64_t)grp * T + t) * 16;
+      int u = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint64_t w = 0;
+        for (int gg = 0; gg < G; ++gg) w |= bm[gg * 4 + i];
+        u += __popcll(w);
+      }
+      p.unique[(int64_t)grp * T + t] = u;
+    }
+  }
   if (p.prob) {  // debug: probabilities from the score pass's exponentials, exp(s - m_t) exp(m_t - m*) / Z
     double* pr = p.prob + bh * p.nk;
     for (int64_t n = tid; n < p.nk; n += THREADS) {

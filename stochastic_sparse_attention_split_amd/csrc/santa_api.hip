@@ -37,7 +37,8 @@ constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-  size_t stash, cmax, csum, cdf, cscale, lastpos, partial, idx, unique, sink, sync_err, budget, boff, kfeat, total;
+  size_t stash, cmax, csum, cdf, cscale, lastpos, partial, idx, unique, sink, sync_err, budget, boff, kfeat, bmap,
+      total;
 };
 
 // every region is written by the call before it is read: no initial contents are required
@@ -71,6 +72,7 @@ Layout layout(int64_t B, int64_t nk, int64_t H, int64_t Hkv, int64_t d, int64_t 
   L.budget = take((size_t)(B * H * T) * sizeof(int32_t));
   L.boff = take((size_t)(B * H * T) * sizeof(int32_t));
   L.kfeat = take((size_t)(B * Hkv) * sizeof(int32_t));
+  L.bmap = (mode & 0xFF) == SANTA_FLASH ? take((size_t)(B * Hkv * T) * 16 * sizeof(uint64_t)) : off;
   L.total = off;
   return L;
 }
@@ -245,6 +247,9 @@ int santa_decode_ex(const santa_args* a) {
   p.boff = (int32_t*)(ws + L.boff);
   p.prob = a->prob_out;
   p.kfeat = (int32_t*)(ws + L.kfeat);
+  p.bmap = (uint64_t*)(ws + L.bmap);
+  // S²ANTA-flash with bf16 and G <= 4 on the sequence-major cache: sampled inside the score pass
+  p.fused = p.mode == SANTA_FLASH && p.bf16 && p.G <= 4 && !p.kfm;
 
   hipStream_t stream = (hipStream_t)a->stream;
   Events ev;
@@ -268,7 +273,7 @@ int santa_decode_ex(const santa_args* a) {
   if (cdf_kernel && !prop && (e = launch_chunk_cdf(p, stream)) != hipSuccess)
     return hip_fail(e, "chunk CDF kernel launch");
   if (cdf_kernel && prop && (e = launch_budget(p, stream)) != hipSuccess) return hip_fail(e, "budget kernel launch");
-  if ((e = launch_resolve(p, stream)) != hipSuccess) return hip_fail(e, "resolve kernel launch");
+  if (!p.fused && (e = launch_resolve(p, stream)) != hipSuccess) return hip_fail(e, "resolve kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if ((e = launch_merge(p, stream)) != hipSuccess) return hip_fail(e, "merge kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -298,7 +303,7 @@ int santa_decode_ex(const santa_args* a) {
         if (x != 0) return fail(SANTA_ERR_HIP, "score kernel: an LDS handshake timed out (%d)", x);
     }
     santa_stats* s = a->stats_out;
-    s->launches = cdf_kernel ? 4 : 3;
+    s->launches = p.fused ? 2 : (cdf_kernel ? 4 : 3);
     s->bytes_k = kbytes;
     s->bytes_v = U * a->d * esz;
     s->bytes_qo = 2 * (int64_t)a->batch * a->heads * a->d * esz;

@@ -470,8 +470,16 @@ __device__ inline bool wait_ge(int* ctr, int target) {
 // dimension and the exponential wave adds the two partial rows. HG = 2 (G = 5..8): the pair splits the
 // heads instead (heads 0-3 and 4-7, each over the whole head dimension), each wave writes complete scores
 // and each exponential wave handles heads w - 8 and w - 4.
-template <int D, int HG>
+// FL: S²ANTA-flash kernel 1 ("Stochastic Sparse Attention for Memory-Bound Inference", Section 3.3 and
+// Appendix P, Algorithm 7) fused in: right after a chunk's exponentials, the exponential wave of head g
+// takes the tile's systematic counts with the uniform budget S_tile (c_n = floor(a0 + inv P_n) -
+// floor(a0 + inv P_{n-1}), inv = S_tile / l_t, P the in-chunk prefix it has just formed, a0 from Philox
+// counter (t, h, b, 4)), writes the index slots and the tile's sampled-key bits, and issues the loads of
+// its sampled V rows; one chunk later (the loads have landed meanwhile) it adds count x row into the fp32
+// tile partial and stores it. Only the merge kernel follows: two launches per decode step.
+template <int D, int HG, bool FL>
 __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
+  static_assert(!FL || HG == 1, "the fused S²ANTA-flash form covers G <= 4");
   using Sg = SGeo<D>;
   constexpr int EPL = 8, PPH = Sg::PPH, CPW = Sg::CPW;
   constexpr int KPW = CHUNK / SQUART;  // keys per MFMA wave
@@ -485,6 +493,7 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   __shared__ __align__(16) double qe[HM][D + 2];
   __shared__ double hnorm[HM];
   __shared__ __align__(16) unsigned char qs[1024 * HG];
+  __shared__ int rl[FL ? 4 : 1][FL ? CHUNK : 1];  // fused S²ANTA-flash: sampled rows (key | count << 8) per head
   constexpr int NCTR = 10;
   __shared__ int ctr[NCTR];
   int* ld = &ctr[0];   // [2]
@@ -607,6 +616,45 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
     // priority above the MFMA waves sharing their SIMD, whose instruction stream would otherwise starve them.
     __builtin_amdgcn_s_setprio(2);
     const int g0 = wave - SMFMA;
+    // fused S²ANTA-flash state: V-row loads of the previous chunk still in flight
+    constexpr int LPR = D / 8;     // lanes per V row (16-byte pieces)
+    constexpr int RPI = 64 / LPR;  // rows per load instruction
+    constexpr int NPEND = 4;       // load instructions carried over to the next chunk
+    uint4 vpend[NPEND];
+    float cpend[NPEND];
+    int npend = 0, tpend = -1;
+    const int grp = b * p.Hkv + kv;
+    const int64_t rstride = 2 * p.seq_stride;
+    const char* vgrp = (const char*)p.V + 2 * ((int64_t)b * p.batch_stride + (int64_t)kv * D);
+    // count x row sums of one chunk: reduce the RPI row lanes, store the head's fp32 tile partial
+    auto store_partial = [&](float* acc, int tt) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int o = LPR; o < 64; o <<= 1) acc[e] += __shfl_xor(acc[e], o, 64);
+      if (lane < LPR) {
+        float4* dst = (float4*)(p.partial + (((int64_t)grp * T + tt) * G + g0) * D + lane * 8);
+        dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      }
+    };
+    auto flush = [&]() {
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+      for (int bi = 0; bi < NPEND; ++bi) {
+        if (bi < npend) {  // wave-uniform
+          float v[8];
+          Piece<true>::to_f32(vpend[bi], v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += cpend[bi] * v[e];
+        }
+      }
+      store_partial(acc, tpend);
+      npend = 0;
+      tpend = -1;
+    };
     for (int k = 0; k < n && ok; ++k) {
       ok = wait_ge(pr, SMFMA * (k + 1));  // chunk k's partials are complete
       if (!ok) break;
@@ -675,7 +723,93 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
           for (int i = 0; i < 4; ++i)
             if (4 * lane + i < len) pr[4 * lane + i] = ex[i];
         }
+        if constexpr (FL) {
+          if (tpend >= 0) flush();  // the previous chunk's rows have landed
+          const int St = p.S_tile;
+          const double inv = (double)St / readlane_f64(incl, 63);
+          const double a0 = uniform53(p.seed, (uint32_t)t, (uint32_t)(h0 + g), (uint32_t)b, TAG_FLASH);
+          // the prefix value before each key: the stored prefix of the previous key (0 before key 0)
+          double prevP = __shfl_up(excl + pre[3], 1, 64);
+          if (lane == 0) prevP = 0.0;
+          int32_t* idst = p.idx + bh * p.L + (int64_t)t * St;
+          int cn[4];
+          uint64_t bm[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const double P = excl + pre[i];
+            const int lo = (int)floor(a0 + inv * prevP), hi = (int)floor(a0 + inv * P);
+            int c = hi > lo ? hi - lo : 0;
+            if (4 * lane + i >= len) c = 0;
+            for (int j = 0; j < c; ++j)
+              if (lo + j < St) idst[lo + j] = (int32_t)(n0 + 4 * lane + i);
+            cn[i] = c;
+            prevP = P;
+            bm[i] = __ballot(c > 0);
+          }
+          if (lane == 0) {
+            uint64_t* bd = p.bmap + (((int64_t)grp * T + t) * 4 + g) * 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bd[i] = bm[i];
+          }
+          // this head's sampled rows in key-slot order (i-major), then their loads
+          int nrows = 0, pos = -1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (cn[i] > 0) {
+              pos = nrows + __popcll(bm[i] & ((1ull << lane) - 1ull));
+              rl[g][pos] = (4 * lane + i) | (cn[i] << 8);
+            }
+            nrows += __popcll(bm[i]);
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const int r = lane / LPR, pcs = lane % LPR;
+          const char* vch = vgrp + n0 * rstride + pcs * 16;
+          if (nrows <= NPEND * RPI) {
+            npend = (nrows + RPI - 1) / RPI;
+            tpend = t;
+#pragma unroll
+            for (int bi = 0; bi < NPEND; ++bi) {
+              if (bi < npend) {  // wave-uniform
+                const int row = bi * RPI + r;
+                const int ent = rl[g][min(row, nrows - 1)];  // rows past the list re-read its last row
+                cpend[bi] = row < nrows ? (float)(ent >> 8) : 0.0f;
+                vpend[bi] = load_stream16(vch + (ent & 255) * rstride);
+              }
+            }
+          } else {  // many sampled rows: gathered here
+            float acc[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+            for (int r0 = 0; r0 < nrows; r0 += RPI * NPEND) {
+              uint4 w[NPEND];
+              float cw[NPEND];
+#pragma unroll
+              for (int bi = 0; bi < NPEND; ++bi) {
+                const int row = r0 + bi * RPI + r;
+                const int ent = rl[g][min(row, nrows - 1)];
+                cw[bi] = row < nrows ? (float)(ent >> 8) : 0.0f;
+                w[bi] = load_stream16(vch + (ent & 255) * rstride);
+              }
+#pragma unroll
+              for (int bi = 0; bi < NPEND; ++bi) {
+                float v[8];
+                Piece<true>::to_f32(w[bi], v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += cw[bi] * v[e];
+              }
+            }
+            store_partial(acc, t);
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // the list is rewritten next chunk
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
       }
+    }
+    if constexpr (FL) {
+      if (tpend >= 0) flush();
     }
     finish();
     return;
@@ -743,10 +877,11 @@ hipError_t launch_d(const Problem& p, hipStream_t st) {
   if constexpr (BF16) {
     const dim3 grid(p.score_blocks_per_group, p.Hkv, p.B);
     if (p.G <= 4) {
-      score_stream_kernel<D, 1><<<grid, STHREADS, 0, st>>>(p);
+      if (p.fused) score_stream_kernel<D, 1, true><<<grid, STHREADS, 0, st>>>(p);
+      else score_stream_kernel<D, 1, false><<<grid, STHREADS, 0, st>>>(p);
       return hipGetLastError();
     }
-    score_stream_kernel<D, 2><<<grid, STHREADS, 0, st>>>(p);
+    score_stream_kernel<D, 2, false><<<grid, STHREADS, 0, st>>>(p);
     return hipGetLastError();
   }
   return p.G <= 4 ? launch_q<D, BF16, 1>(p, st) : launch_q<D, BF16, 2>(p, st);
