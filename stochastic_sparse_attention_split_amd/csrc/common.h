@@ -326,6 +326,8 @@ struct Problem {
   double* prob;          // optional [B, H, nk]
   int32_t* kfeat;        // [B, Hkv] feature rows of K^T read by the feature-major score pass
   bool fused;            // S²ANTA-flash sampled and gathered inside the streaming score pass
+  bool want_unique;      // fill unique[] (the stats path reads it); the fused S²ANTA-flash skips it otherwise
+  bool want_idx;         // the caller asked for idx_out (the fused S²ANTA-flash writes idx only then)
   uint64_t* bmap;        // [B, Hkv, T, 4, 4] fused S²ANTA-flash: sampled keys of each (chunk, head) as bits
 };
 

@@ -695,7 +695,7 @@ __global__ __launch_bounds__(THREADS) void merge_flash_kernel(Problem p) {
     else
       ((float*)p.out)[o] = (float)r;
   }
-  if (p.fused && g == 0) {  // the group's distinct sampled keys per chunk: union of its heads' key bits
+  if (p.fused && p.want_unique && g == 0) {  // distinct sampled keys per chunk: union of the heads' key bits
     const int grp = b * p.Hkv + kv;
     for (int t = tid; t < T; t += THREADS) {
       const uint64_t* bm = p.bmap + ((int64_t)grp * T + t) * 16;

@@ -250,6 +250,8 @@ int santa_decode_ex(const santa_args* a) {
   p.bmap = (uint64_t*)(ws + L.bmap);
   // S²ANTA-flash with bf16 and G <= 4 on the sequence-major cache: sampled inside the score pass
   p.fused = p.mode == SANTA_FLASH && p.bf16 && p.G <= 4 && !p.kfm;
+  p.want_unique = a->stats_out != nullptr;
+  p.want_idx = a->idx_out != nullptr;
 
   hipStream_t stream = (hipStream_t)a->stream;
   Events ev;

@@ -709,10 +709,13 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
         const double incl = wave_incl_scan_dpp(run);
         double excl = __shfl_up(incl, 1, 64);
         if (lane == 0) excl = 0.0;
-        // stash rows are CHUNK-padded: the whole chunk is stored, keys past the end repeat the total
-        double2* dst = (double2*)(p.stash + bh * p.stash_stride + n0 + 4 * lane);
-        dst[0] = make_double2(excl + pre[0], excl + pre[1]);
-        dst[1] = make_double2(excl + pre[2], excl + pre[3]);
+        // stash rows are CHUNK-padded: the whole chunk is stored, keys past the end repeat the total (the
+        // fused S²ANTA-flash samples here and needs no stash)
+        if constexpr (!FL) {
+          double2* dst = (double2*)(p.stash + bh * p.stash_stride + n0 + 4 * lane);
+          dst[0] = make_double2(excl + pre[0], excl + pre[1]);
+          dst[1] = make_double2(excl + pre[2], excl + pre[3]);
+        }
         if (lane == 0) {
           p.cmax[bh * T + t] = m;
           p.csum[bh * T + t] = readlane_f64(incl, 63);
@@ -740,13 +743,14 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
             const int lo = (int)floor(a0 + inv * prevP), hi = (int)floor(a0 + inv * P);
             int c = hi > lo ? hi - lo : 0;
             if (4 * lane + i >= len) c = 0;
-            for (int j = 0; j < c; ++j)
-              if (lo + j < St) idst[lo + j] = (int32_t)(n0 + 4 * lane + i);
+            if (p.want_idx)
+              for (int j = 0; j < c; ++j)
+                if (lo + j < St) idst[lo + j] = (int32_t)(n0 + 4 * lane + i);
             cn[i] = c;
             prevP = P;
             bm[i] = __ballot(c > 0);
           }
-          if (lane == 0) {
+          if (p.want_unique && lane == 0) {
             uint64_t* bd = p.bmap + (((int64_t)grp * T + t) * 4 + g) * 4;
 #pragma unroll
             for (int i = 0; i < 4; ++i) bd[i] = bm[i];
