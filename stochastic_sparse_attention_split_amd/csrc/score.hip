@@ -7,7 +7,11 @@
 // exp(s_{h,n} - m_{h,t}). This pass stores their in-chunk inclusive prefix sums (the chunk's CDF up to
 // the chunk's own scale) and l_{h,t} = the chunk total, which is what the sampler's inverse CDF needs.
 //
-// MI355X design:
+// Two forms. The streaming form (bf16 caches, the usual case; described above score_stream_kernel)
+// copies K tiles into LDS with global_load_lds and splits the work into copy, matrix-core and
+// exponential waves. The register form below (fp32 caches) works as follows.
+//
+// MI355X design of the register form:
 //   * K is streamed once with non-temporal 16-byte loads in full-row order (16 lanes cover a 256-byte
 //     row), the next chunk's loads in flight while the current chunk is computed. The current chunk
 //     sits in a padded LDS tile (row stride + 16 bytes), from which the matrix-core layout is read
@@ -446,7 +450,7 @@ __device__ inline bool wait_ge(int* ctr, int target) {
   return true;
 }
 
-// Streaming score pass for bf16 caches and G <= 4, one block of 16 waves per CU, three roles that meet
+// Streaming score pass for bf16 caches and G <= 8, one block of 16 waves per CU, three roles that meet
 // only through LDS counters (no block-wide barrier after the start), so the K stream, the matrix cores
 // and the exponentials overlap:
 //   * waves 0..7 (two per SIMD): fp64 MFMA over key quarter w & 3 (64 keys: four 16-key groups) and
