@@ -198,6 +198,17 @@ def test_flash_cases(case):
         assert idx.shape[2] == T * r.extra["S_tile"]
 
 
+def test_flash_launch_count():
+    """S²ANTA-flash samples inside the score pass for bf16 caches with G <= 4 (two launches: score pass and
+    merge); fp32 and G > 4 keep the separate sampling kernel (three launches)."""
+    dev = torch.device("cuda:0")
+    for (H, Hkv, dtype, want) in ((8, 2, "bf16", 2), (8, 2, "f32", 3), (12, 2, "bf16", 3)):
+        q, K, V, _ = workloads.make_inputs(1, H, Hkv, 64, 1500, dtype=dtype, spikes_per_head=2, rng_seed=H)
+        _, info = santa.decode(q.to(dev), K.to(dev), V.to(dev), 40, "flash", 1, stats=True)
+        log(f"flash H{H}/{Hkv} {dtype}: {info['launches']} launches")
+        assert info["launches"] == want
+
+
 @pytest.mark.parametrize("S", [256, 2048])
 def test_flash_workload_2(S):
     """S²ANTA-flash on the 32k Llama-3.1-8B-shaped layer; S = 2048 is the accuracy-matching budget the paper
