@@ -42,8 +42,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--no-prop", action="store_true", help="skip the S2ANTA-prop (S=128) and S2ANTA-flash "
-                                                           "(S=2048) measurements")
+    ap.add_argument("--no-prop", action="store_true", help="skip the S2ANTA-prop (S=128), S2ANTA-flash "
+                                                           "(S=2048), feature-major and head-parallel share "
+                                                           "measurements")
     ap.add_argument("--profile-steps", action="store_true", help="minimal run for profilers: no CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 64 MiB device copies (scale reference for hardware byte counters)")
@@ -217,6 +218,42 @@ def main():
                        "k_rows_read_fraction": round(inf["bytes_k"] / info["bytes_k"], 4)}
         del Kt
 
+    tp = None
+    if not args.no_prop and w.Hkv % 8 == 0:  # one GPU's share of an 8-way head-parallel split, own cache
+        hk, G = w.Hkv // 8, w.H // w.Hkv
+        q8 = q[:, :hk * G].contiguous()
+        K8, V8 = K[:, :, :hk].contiguous(), V[:, :, :hk].contiguous()
+        out8, dout8 = torch.empty_like(q8), torch.empty_like(q8)
+        ws8 = santa.new_workspace(santa.workspace_bytes(w.B, w.nk, hk * G, hk, w.d, w.S), dev)
+        dws8 = torch.empty(santa.dense_workspace_bytes(w.B, w.nk, hk * G, hk, w.d), dtype=torch.uint8, device=dev)
+
+        def tp_step():
+            santa.decode(q8, K8, V8, w.S, w.mode, w.seed, ternary=ternary, out=out8, workspace=ws8, stream=stream)
+
+        def tp_dense():
+            santa.dense_decode(q8, K8, V8, out=dout8, workspace=dws8, stream=stream)
+
+        for _ in range(args.warmup):
+            tp_step()
+            tp_dense()
+        tp_us = timed(tp_step, args.steps, cold=True)
+        tpd_us = timed(tp_dense, args.steps, cold=True)
+        _, inf8 = santa.decode(q8, K8, V8, w.S, w.mode, w.seed, ternary=ternary, out=out8, workspace=ws8,
+                               stats=True)
+        tp = {"heads": hk * G, "kv_heads": hk, "us_median": round(statistics.median(tp_us), 3),
+              "launches": int(inf8["launches"]), "bytes_k": int(inf8["bytes_k"]),
+              "dense_bf16_us_median": round(statistics.median(tpd_us), 3)}
+        tp["speedup_vs_dense"] = round(tp["dense_bf16_us_median"] / tp["us_median"], 3)
+        del q8, K8, V8, ws8, dws8
+
+    # the device's streaming read rate on the same K bytes under the same cold protocol: the practical
+    # ceiling of the score pass's HBM stream, beside the published peak
+    rscratch = torch.empty(int(santa.lib().santa_stream_read_scratch_bytes()), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        santa.stream_read(K, rscratch, stream)
+    read_us = timed(lambda: santa.stream_read(K, rscratch, stream), args.steps, cold=True)
+    read_GBps = K.numel() * K.element_size() / (statistics.median(read_us) * 1e-6) / 1e9
+
     dense_us = None
     if not args.no_dense:
         for _ in range(args.warmup):
@@ -273,7 +310,11 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
+            "measured_read_peak": round(read_GBps, 1),
+            "frac_of_measured_read_peak": round(achieved / read_GBps, 4),
         },
+        "stream_read_K": {"bytes": int(K.numel() * K.element_size()), "us_median": round(statistics.median(read_us), 3),
+                          "GBps": round(read_GBps, 1)},
     }
     if dense_us is not None:
         dmed = statistics.median(dense_us)
@@ -291,6 +332,9 @@ def main():
         res["s2anta_flash_S2048"] = {"us_median": round(fmed, 3), "us_mean": round(statistics.fmean(flash_us), 3)}
         if dense_us is not None:
             res["s2anta_flash_S2048"]["speedup_vs_dense"] = round(statistics.median(dense_us) / fmed, 3)
+
+    if tp is not None:
+        res["head_parallel_share_of_8"] = tp
 
     if args.copy_calibration:
         src = torch.ones((64 << 20) // 4, dtype=torch.float32, device=dev)

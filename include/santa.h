@@ -177,6 +177,16 @@ size_t santa_dense_workspace_bytes(int batch, int64_t nk, int heads, int kv_head
  */
 void santa_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
 
+/*
+ * santa_stream_read — diagnostic: reads `bytes` of device memory at `src` once with the 16-byte
+ * non-temporal loads the score pass uses for K, writing one XOR word per block into `scratch` (device
+ * memory of santa_stream_read_scratch_bytes() bytes, contents meaningless). Timed around the call on
+ * the caller's stream, it measures the read bandwidth the device reaches for that size and cache state.
+ * bytes must be a positive multiple of 16 and src 16-byte aligned; asynchronous like the decode calls.
+ */
+int santa_stream_read(const void* src, size_t bytes, void* scratch, size_t scratch_bytes, void* stream);
+size_t santa_stream_read_scratch_bytes(void);
+
 const char* santa_status_string(int status);
 const char* santa_last_error(void);   /* thread-local description of the last failure, "" if none */
 const char* santa_version(void);

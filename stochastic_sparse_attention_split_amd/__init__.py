@@ -36,7 +36,8 @@ MODES = {"iid": IID, "strat": STRAT, "sys": SYS, "prop": PROP, "flash": FLASH}
 EXPORTED = [
     "santa_decode", "santa_decode_ex", "santa_workspace_bytes", "santa_dense_decode",
     "santa_dense_workspace_bytes", "santa_philox4x32_10", "santa_status_string", "santa_last_error",
-    "santa_version", "santa_release", "santa_samples_per_head",
+    "santa_version", "santa_release", "santa_samples_per_head", "santa_stream_read",
+    "santa_stream_read_scratch_bytes",
 ]
 
 
@@ -101,6 +102,11 @@ def lib() -> ctypes.CDLL:
         L.santa_version.argtypes = []
         L.santa_release.restype = None
         L.santa_release.argtypes = []
+        L.santa_stream_read.restype = ctypes.c_int
+        L.santa_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]
+        L.santa_stream_read_scratch_bytes.restype = ctypes.c_size_t
+        L.santa_stream_read_scratch_bytes.argtypes = []
         _lib = L
     return _lib
 
@@ -282,6 +288,22 @@ def dense_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, *, nk: int |
     a.workspace_bytes = workspace.numel() * workspace.element_size()
     _check(lib().santa_dense_decode(ctypes.byref(a)))
     return out
+
+
+def stream_read(t: torch.Tensor, scratch: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Reads the bytes of a contiguous device tensor once through santa_stream_read (a bandwidth probe);
+    returns the scratch tensor holding one XOR word per block."""
+    if not t.is_contiguous():
+        raise ValueError("stream_read needs a contiguous tensor")
+    need = int(lib().santa_stream_read_scratch_bytes())
+    if scratch is None:
+        scratch = torch.empty(need, dtype=torch.uint8, device=t.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    st = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    _check(lib().santa_stream_read(t.data_ptr(), t.numel() * t.element_size(), scratch.data_ptr(),
+                                   scratch.numel() * scratch.element_size(), st))
+    return scratch
 
 
 def philox4x32_10(ctr, key):

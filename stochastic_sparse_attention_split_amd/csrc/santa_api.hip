@@ -435,6 +435,23 @@ int santa_dense_decode(const santa_args* a) {
 
 // ---- diagnostics
 
+size_t santa_stream_read_scratch_bytes(void) { return (size_t)STREAM_READ_MAX_BLOCKS * sizeof(uint32_t); }
+
+int santa_stream_read(const void* src, size_t bytes, void* scratch, size_t scratch_bytes, void* stream) {
+  g_err.clear();
+  if (!src || !scratch) return fail(SANTA_ERR_INVALID_ARG, "src and scratch must be non-NULL");
+  if (bytes < 16 || bytes % 16 || (uintptr_t)src % 16)
+    return fail(SANTA_ERR_INVALID_ARG, "bytes (%zu) must be a positive multiple of 16 and src 16-byte aligned", bytes);
+  if (scratch_bytes < santa_stream_read_scratch_bytes())
+    return fail(SANTA_ERR_WORKSPACE, "scratch of %zu bytes is smaller than the %zu needed", scratch_bytes,
+                santa_stream_read_scratch_bytes());
+  (void)hipGetLastError();
+  const int blocks = stream_read_blocks((int64_t)bytes, device_cus());
+  const hipError_t e = launch_stream_read(src, (int64_t)bytes, (uint32_t*)scratch, blocks, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "stream read kernel launch");
+  return SANTA_OK;
+}
+
 void santa_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
   const Philox4 r = philox4x32_10(ctr[0], ctr[1], ctr[2], ctr[3], key[0], key[1]);
   out[0] = r.x0;

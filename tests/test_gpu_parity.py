@@ -220,6 +220,28 @@ def test_flash_workload_2(S):
     assert rep["mismatches"] == 0
 
 
+@pytest.mark.parametrize("mode,S", [("strat", 256), ("prop", 128), ("flash", 2048)])
+def test_head_parallel_share_of_workload_2(mode, S):
+    """One GPU's share of an 8-way head-parallel split of the 32k Llama-3.1-8B-shaped layer: the first KV
+    group and its 4 query heads in a cache of their own. Against the oracle, and bit-identical to the same
+    heads of the whole-layer call: every kernel is local to a (sequence, KV group) unit."""
+    w = workloads.make(2)
+    G = w.H // w.Hkv
+    q8 = w.q[:, :G].contiguous()
+    K8, V8 = w.K[:, :, :1].contiguous(), w.V[:, :, :1].contiguous()
+    log(f"head-parallel share of {w.name}: H{G}/Hkv1 nk{w.nk} {mode} S={S}")
+    rep, _, out8, idx8 = compare(q8, K8, V8, S, mode, w.seed, dtype=w.dtype, want_prob=False,
+                                 label=f"{w.name} share {mode} S={S}")
+    log(f"  {rep}")
+    assert rep["mismatches"] == 0
+    dev = torch.device("cuda:0")
+    L = santa.samples_per_head(w.nk, S, mode)
+    idx = torch.empty((w.B, w.H, L), dtype=torch.int32, device=dev)
+    out = santa.decode(w.q.to(dev), w.K.to(dev), w.V.to(dev), S, mode, w.seed, idx_out=idx)
+    assert torch.equal(out[:, :G].cpu(), out8.cpu())
+    assert torch.equal(idx[:, :G].cpu(), idx8.cpu())
+
+
 FM_CASES = [
     # B, H, Hkv, d, nk, dtype, S, mode, ternary, group B, spikes  (feature-major K^T; Section 5.1, App. C.2)
     (1, 4, 1, 128, 1000, "bf16", 64, "strat", False, 0, 2),     # exact scores from K^T
@@ -401,8 +423,11 @@ def test_dense_baseline_matches_oracle():
     log("dense baseline")
     dev = torch.device("cuda:0")
     for (B, H, Hkv, d, nk, dtype) in [(1, 32, 8, 128, 32768, "bf16"), (2, 7, 1, 64, 1500, "bf16"),
-                                      (1, 4, 2, 128, 1000, "f32")]:
-        q, K, V, _ = workloads.make_inputs(B, H, Hkv, d, nk, dtype=dtype, spikes_per_head=4, rng_seed=nk)
+                                      (1, 4, 2, 128, 1000, "f32"), (1, 16, 2, 128, 3001, "bf16"),
+                                      (2, 8, 2, 64, 257, "f32"), (1, 8, 1, 64, 1, "bf16"),
+                                      (1, 2, 2, 128, 70000, "f32")]:
+        q, K, V, _ = workloads.make_inputs(B, H, Hkv, d, nk, dtype=dtype, spikes_per_head=min(4, nk * Hkv // H),
+                                           rng_seed=nk)
         out = santa.dense_decode(q.to(dev), K.to(dev), V.to(dev))
         torch.cuda.synchronize()
         mu, mu_r = oracle.dense(q.float().numpy(), K.float().numpy(), V.float().numpy(), out_dtype=dtype)
@@ -429,3 +454,19 @@ def test_gpu_estimator_unbiased_4096_seeds():
     mu = p @ Vf
     vt = oracle.var_trace_iid(p, Vf, w.S)
     assert np.linalg.norm(ests.mean(axis=0) - mu) <= 3 * np.sqrt(vt / 4096)
+
+
+def test_stream_read_probe_reads_every_byte():
+    """The bandwidth probe folds every 32-bit word of the buffer: the XOR of its per-block words equals the
+    XOR of the whole buffer, for sizes from one 16-byte piece to a 64 MiB cache."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(5)
+    for n in (4, 4 * 257, 1 << 18, (1 << 24) + 4):
+        t = torch.randint(-(1 << 31), (1 << 31) - 1, (n,), dtype=torch.int32, generator=g)
+        want = int(np.bitwise_xor.reduce(t.numpy().view(np.uint32)))
+        scratch = torch.zeros(int(santa.lib().santa_stream_read_scratch_bytes()), dtype=torch.uint8, device=dev)
+        santa.stream_read(t.to(dev), scratch)
+        got = int(np.bitwise_xor.reduce(scratch.cpu().numpy().view(np.uint32)))
+        log(f"stream read {n * 4} bytes: xor {got:#010x} want {want:#010x}")
+        assert got == want
+
