@@ -9,8 +9,10 @@ launching stream. Before every timed step a 1 GiB in-place update evicts K/V fro
 256 MB Infinity Cache would otherwise hold the 64 MiB K), outside the events, like the cold-cache
 protocol of the paper's kernel benchmark (Appendix Q). Reported alongside:
   * the dense bf16 decode baseline of the same library on the same inputs and protocol;
-  * per-kernel times from events between the launches (a separate pass), giving the roofline of the
-    dominant kernel (the score pass: algorithmic bytes = K + q per launch);
+  * per-stage times (a separate pass, same protocol): the score kernel's execution time from HIP events
+    recorded at the kernel's own start and end on the launching stream, which gives the roofline of the
+    dominant kernel (the score pass: algorithmic bytes = K + q per launch), and the later stages from
+    events between the launches;
   * the fp64 oracle timed on the host's cores on the same inputs (a baseline, not the target).
 
 Prints one JSON line. --gpus N > 1 is refused: the benchmark runs on one GPU.

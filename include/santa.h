@@ -124,8 +124,11 @@ typedef struct santa_args {
                                 for SANTA_FLASH): sampled key index of each point, in point order */
   double* prob_out;          /* device [batch, heads, nk]: softmax probabilities */
   santa_stats* stats_out;    /* host; the call synchronises the stream to fill it */
-  float* stage_ms;           /* host float[4]: GPU time of [score, chunk CDF + resolve, merge, whole call]
-                                from events between the launches; synchronises the stream */
+  float* stage_ms;           /* host float[4], milliseconds; synchronises the stream. [0]: execution time of
+                                the score kernel (events HIP records at the kernel's own start and end);
+                                [1]: from the end of the score kernel to an event after the chunk CDF and
+                                resolve launches; [2]: from there to an event after the merge launch;
+                                [3]: from the score kernel's start to that last event */
   /* SANTA_K_FEATURE_MAJOR only (elements); rows must hold at least nk rounded up to 8 and start 16-byte
      aligned */
   int64_t kt_row_stride;     /* between feature rows; 0 means nk rounded up to 8 */

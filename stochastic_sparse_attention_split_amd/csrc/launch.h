@@ -1,14 +1,32 @@
 // Host-side launchers of the HIP kernels (one per translation unit); each returns the launch status.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "common.h"
 
 namespace santa {
 
-hipError_t launch_score(const Problem& p, hipStream_t st);     // score.hip
-hipError_t launch_score_fm(const Problem& p, hipStream_t st);  // score_fm.hip: feature-major K^T
+// Optional timing events of one launch. When set, HIP records them at the kernel's own start and end
+// (hipExtLaunchKernel), so their elapsed time is the kernel's execution without the gaps around it.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+template <typename... Args>
+hipError_t launch_timed(void (*k)(Args...), dim3 grid, dim3 block, hipStream_t st, const LaunchEvents& ev,
+                        Args... args) {
+  if (ev.start)
+    hipExtLaunchKernelGGL(k, grid, block, 0, st, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(k, grid, block, 0, st, args...);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const Problem& p, hipStream_t st, const LaunchEvents& ev = {});     // score.hip
+hipError_t launch_score_fm(const Problem& p, hipStream_t st, const LaunchEvents& ev = {});  // score_fm.hip: K^T
 int score_blocks_per_cu(int d, bool bf16, int G);              // resident score blocks per CU (LDS)
 hipError_t launch_chunk_cdf(const Problem& p, hipStream_t st); // score.hip
 hipError_t launch_budget(const Problem& p, hipStream_t st);    // prop.hip: S²ANTA-prop tile budgets

@@ -263,11 +263,12 @@ int santa_decode_ex(const santa_args* a) {
     }
   }
   hipError_t e;
-  if (ev.on && (e = hipEventRecord(ev.e[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   (void)hipGetLastError();  // start from a clean error state
-  if ((e = p.kfm ? launch_score_fm(p, stream) : launch_score(p, stream)) != hipSuccess)
+  // with stage timing, HIP records e[0] and e[1] at the score kernel's own start and end
+  LaunchEvents sev;
+  if (ev.on) sev = LaunchEvents{ev.e[0], ev.e[1]};
+  if ((e = p.kfm ? launch_score_fm(p, stream, sev) : launch_score(p, stream, sev)) != hipSuccess)
     return hip_fail(e, "score kernel launch");
-  if (ev.on && (e = hipEventRecord(ev.e[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   const bool prop = p.mode == SANTA_PROP;
   // for T <= FUSED_CDF_MAX_T the sampling kernel builds the chunk CDF (or the prop tile budgets) itself;
   // S²ANTA-flash needs neither

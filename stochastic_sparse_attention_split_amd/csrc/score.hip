@@ -874,25 +874,23 @@ constexpr int blocks_per_cu() {
 }
 
 template <int D, bool BF16, int NQ>
-hipError_t launch_q(const Problem& p, hipStream_t st) {
+hipError_t launch_q(const Problem& p, hipStream_t st, const LaunchEvents& ev) {
   constexpr int MINB = blocks_per_cu<D, BF16, NQ>();
-  score_kernel<D, BF16, NQ, MINB><<<dim3(p.score_blocks_per_group, p.Hkv, p.B), THREADS, 0, st>>>(p);
-  return hipGetLastError();
+  return launch_timed(score_kernel<D, BF16, NQ, MINB>, dim3(p.score_blocks_per_group, p.Hkv, p.B), dim3(THREADS), st,
+                      ev, p);
 }
 
 template <int D, bool BF16>
-hipError_t launch_d(const Problem& p, hipStream_t st) {
+hipError_t launch_d(const Problem& p, hipStream_t st, const LaunchEvents& ev) {
   if constexpr (BF16) {
     const dim3 grid(p.score_blocks_per_group, p.Hkv, p.B);
     if (p.G <= 4) {
-      if (p.fused) score_stream_kernel<D, 1, true><<<grid, STHREADS, 0, st>>>(p);
-      else score_stream_kernel<D, 1, false><<<grid, STHREADS, 0, st>>>(p);
-      return hipGetLastError();
+      if (p.fused) return launch_timed(score_stream_kernel<D, 1, true>, grid, dim3(STHREADS), st, ev, p);
+      return launch_timed(score_stream_kernel<D, 1, false>, grid, dim3(STHREADS), st, ev, p);
     }
-    score_stream_kernel<D, 2, false><<<grid, STHREADS, 0, st>>>(p);
-    return hipGetLastError();
+    return launch_timed(score_stream_kernel<D, 2, false>, grid, dim3(STHREADS), st, ev, p);
   }
-  return p.G <= 4 ? launch_q<D, BF16, 1>(p, st) : launch_q<D, BF16, 2>(p, st);
+  return p.G <= 4 ? launch_q<D, BF16, 1>(p, st, ev) : launch_q<D, BF16, 2>(p, st, ev);
 }
 
 }  // namespace
@@ -908,9 +906,9 @@ int score_blocks_per_cu(int d, bool bf16, int G) {
   return q1 ? blocks_per_cu<64, false, 1>() : blocks_per_cu<64, false, 2>();
 }
 
-hipError_t launch_score(const Problem& p, hipStream_t st) {
-  if (p.d == 128) return p.bf16 ? launch_d<128, true>(p, st) : launch_d<128, false>(p, st);
-  return p.bf16 ? launch_d<64, true>(p, st) : launch_d<64, false>(p, st);
+hipError_t launch_score(const Problem& p, hipStream_t st, const LaunchEvents& ev) {
+  if (p.d == 128) return p.bf16 ? launch_d<128, true>(p, st, ev) : launch_d<128, false>(p, st, ev);
+  return p.bf16 ? launch_d<64, true>(p, st, ev) : launch_d<64, false>(p, st, ev);
 }
 
 hipError_t launch_chunk_cdf(const Problem& p, hipStream_t st) {

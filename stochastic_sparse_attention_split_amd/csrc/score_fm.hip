@@ -232,26 +232,25 @@ __global__ __launch_bounds__(FM_THREADS) void score_fm_kernel(Problem p) {
 }
 
 template <int D, bool BF16, int GM, int KPT>
-hipError_t launch_fm(const Problem& p, hipStream_t st) {
+hipError_t launch_fm(const Problem& p, hipStream_t st, const LaunchEvents& ev) {
   constexpr int CPB = 64 * KPT / CHUNK;
   const dim3 grid((p.T + CPB - 1) / CPB, p.Hkv, p.B);
-  score_fm_kernel<D, BF16, GM, KPT><<<grid, FM_THREADS, 0, st>>>(p);
-  return hipGetLastError();
+  return launch_timed(score_fm_kernel<D, BF16, GM, KPT>, grid, dim3(FM_THREADS), st, ev, p);
 }
 
 template <int D, bool BF16>
-hipError_t launch_fm_dt(const Problem& p, hipStream_t st) {
+hipError_t launch_fm_dt(const Problem& p, hipStream_t st, const LaunchEvents& ev) {
   // bf16 with G <= 4: 8 keys per thread (one 16-byte load per feature row); otherwise 4 keys per thread
-  if (p.G > 4) return launch_fm<D, BF16, 8, 4>(p, st);
-  if constexpr (BF16) return launch_fm<D, BF16, 4, 8>(p, st);
-  else return launch_fm<D, BF16, 4, 4>(p, st);
+  if (p.G > 4) return launch_fm<D, BF16, 8, 4>(p, st, ev);
+  if constexpr (BF16) return launch_fm<D, BF16, 4, 8>(p, st, ev);
+  else return launch_fm<D, BF16, 4, 4>(p, st, ev);
 }
 
 }  // namespace
 
-hipError_t launch_score_fm(const Problem& p, hipStream_t st) {
-  if (p.d == 128) return p.bf16 ? launch_fm_dt<128, true>(p, st) : launch_fm_dt<128, false>(p, st);
-  return p.bf16 ? launch_fm_dt<64, true>(p, st) : launch_fm_dt<64, false>(p, st);
+hipError_t launch_score_fm(const Problem& p, hipStream_t st, const LaunchEvents& ev) {
+  if (p.d == 128) return p.bf16 ? launch_fm_dt<128, true>(p, st, ev) : launch_fm_dt<128, false>(p, st, ev);
+  return p.bf16 ? launch_fm_dt<64, true>(p, st, ev) : launch_fm_dt<64, false>(p, st, ev);
 }
 
 }  // namespace santa
