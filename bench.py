@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--S", type=int, default=None, help="sample count override (the workload's own S by default)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -132,7 +133,7 @@ def main():
         print(json.dumps(run_sweep(args, santa, workloads, torch, np, dev)), flush=True)
         return
 
-    w = workloads.make(args.config)
+    w = workloads.make(args.config, S=args.S)
     q, K, V = w.q.to(dev), w.K.to(dev), w.V.to(dev)
     ternary = w.ternary
     out = torch.empty_like(q)

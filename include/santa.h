@@ -181,6 +181,14 @@ size_t santa_dense_workspace_bytes(int batch, int64_t nk, int heads, int kv_head
 void santa_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
 
 /*
+ * santa_exp_f64 — host-side evaluation of the library's own fp64 exponential (the same inline code the
+ * kernels run for every softmax weight exp(s - max) and chunk scale exp(m_t - m*), Section 2, Eq. 1), for
+ * accuracy tests: e^x within a few units in the last place for -746 <= x <= 709, +0 below -746 and for
+ * -inf, exactly 1 at 0. No GPU is touched.
+ */
+double santa_exp_f64(double x);
+
+/*
  * santa_stream_read — diagnostic: reads `bytes` of device memory at `src` once with the 16-byte
  * non-temporal loads the score pass uses for K, writing one XOR word per block into `scratch` (device
  * memory of santa_stream_read_scratch_bytes() bytes, contents meaningless). Timed around the call on

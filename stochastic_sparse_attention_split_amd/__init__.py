@@ -35,7 +35,7 @@ MODES = {"iid": IID, "strat": STRAT, "sys": SYS, "prop": PROP, "flash": FLASH}
 
 EXPORTED = [
     "santa_decode", "santa_decode_ex", "santa_workspace_bytes", "santa_dense_decode",
-    "santa_dense_workspace_bytes", "santa_philox4x32_10", "santa_status_string", "santa_last_error",
+    "santa_dense_workspace_bytes", "santa_philox4x32_10", "santa_exp_f64", "santa_status_string", "santa_last_error",
     "santa_version", "santa_release", "santa_samples_per_head", "santa_stream_read",
     "santa_stream_read_scratch_bytes",
 ]
@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.santa_dense_workspace_bytes.restype = ctypes.c_size_t
         L.santa_dense_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                                   ctypes.c_int]
+        L.santa_exp_f64.restype = ctypes.c_double
+        L.santa_exp_f64.argtypes = [ctypes.c_double]
         L.santa_philox4x32_10.restype = None
         L.santa_philox4x32_10.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32),
                                           ctypes.POINTER(ctypes.c_uint32)]
@@ -313,6 +315,11 @@ def philox4x32_10(ctr, key):
     o = (ctypes.c_uint32 * 4)()
     lib().santa_philox4x32_10(c, k, o)
     return tuple(int(x) for x in o)
+
+
+def exp_f64(x: float) -> float:
+    """The library's own fp64 exponential evaluated on the host (the kernels' code path)."""
+    return float(lib().santa_exp_f64(float(x)))
 
 
 def release():

@@ -60,6 +60,39 @@ constexpr uint32_t TAG_GROUP = 5;      // mean-group Bernoulli feature m (+256 n
 constexpr uint32_t TAG_BERNOULLI = 2;  // ternary-query element m (+256 n for Bernoulli sample n)
 
 // ---------------------------------------------------------------------------------------------
+// e^x in fp64 for the softmax arguments x = s - max <= 0 (also correct for x up to ~709); x < -746 and
+// x = -inf give +0. Derived from the mathematics: x = k ln2 + r with k = rint(x / ln2), |r| <= ln2 / 2;
+// ln2 = LN2_HI + LN2_LO where LN2_HI keeps 32 significant bits, so k * LN2_HI is exact for |k| < 2^21;
+// e^r by its Taylor series through r^13 (the remainder is below 2^-57 relative on |r| <= ln2 / 2), in
+// Horner form with the coefficients 1/n! rounded to fp64; then the factor 2^k by ldexp. Straight-line
+// code with no branch: a call costs 19 fp64 operations. Accuracy: within a few units in the last place of
+// the correctly rounded result; e^0 = 1 exactly.
+__host__ __device__ inline double exp_f64(double x) {
+  constexpr double INV_LN2 = 0x1.71547652b82fep+0;   // 1 / ln 2
+  constexpr double LN2_HI = 0x1.62e42ff000000p-1;    // ln 2 to 32 significant bits
+  constexpr double LN2_LO = -0x1.718432a1b0e26p-35;  // ln 2 - LN2_HI
+  const double k = fmax(rint(x * INV_LN2), -1100.0);  // -inf and huge negative x: clamped (result 0 below)
+  double r = fma(-k, LN2_HI, x);
+  r = fma(-k, LN2_LO, r);
+  double q = 0x1.6124613a86d09p-33;       // 1/13!
+  q = fma(q, r, 0x1.1eed8eff8d898p-29);   // 1/12!
+  q = fma(q, r, 0x1.ae64567f544e4p-26);   // 1/11!
+  q = fma(q, r, 0x1.27e4fb7789f5cp-22);   // 1/10!
+  q = fma(q, r, 0x1.71de3a556c734p-19);   // 1/9!
+  q = fma(q, r, 0x1.a01a01a01a01ap-16);   // 1/8!
+  q = fma(q, r, 0x1.a01a01a01a01ap-13);   // 1/7!
+  q = fma(q, r, 0x1.6c16c16c16c17p-10);   // 1/6!
+  q = fma(q, r, 0x1.1111111111111p-7);    // 1/5!
+  q = fma(q, r, 0x1.5555555555555p-5);    // 1/4!
+  q = fma(q, r, 0x1.5555555555555p-3);    // 1/3!
+  q = fma(q, r, 0.5);                     // 1/2!
+  q = fma(q, r, 1.0);                     // 1/1!
+  q = fma(q, r, 1.0);                     // 1/0!
+  const double y = ldexp(q, (int)k);
+  return x >= -746.0 ? y : 0.0;
+}
+
+// ---------------------------------------------------------------------------------------------
 // 16-byte streaming load that does not allocate in the caches (K and V are read once per step; a
 // non-temporal load also avoids evicting dirty lines from the Infinity Cache)
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -211,7 +244,7 @@ __device__ inline void chunk_cdf_wave(const double* m, const double* l, int T, i
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const bool valid = t0 + j < T;
-    o.f[j] = valid ? exp(m[j] - ms) : 0.0;
+    o.f[j] = valid ? exp_f64(m[j] - ms) : 0.0;
     const double w = l[j] * o.f[j];
     loc[j] = run;  // local exclusive prefix, offset below
     run += w;

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(BT) void budget_kernel(Problem p) {
   double w[TPT], part = 0.0;
 #pragma unroll
   for (int k = 0; k < TPT; ++k) {
-    const double e = exp(m[k] - ms);
+    const double e = exp_f64(m[k] - ms);
     w[k] = tid + BT * k < T ? e * l[k] : 0.0;
     part += w[k];
     if (tid + BT * k < T) p.cscale[bh * T + tid + BT * k] = e;

@@ -355,7 +355,7 @@ __device__ inline TileBudget tile_budget_wave(const double* m, const double* l, 
   double e[PER], w[PER], run = 0.0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    e[j] = exp(m[j] - ms);
+    e[j] = exp_f64(m[j] - ms);
     w[j] = t0 + j < T ? e[j] * l[j] : 0.0;
     run += w[j];
   }
@@ -650,7 +650,7 @@ __global__ __launch_bounds__(THREADS) void merge_flash_kernel(Problem p) {
   const double ms = block_max_f64<NW>(mx, bred, lane, wave);
   double part = 0.0;
   for (int t = tid; t < T; t += THREADS) {
-    const double w = exp(p.cmax[bh * T + t] - ms) * p.csum[bh * T + t];
+    const double w = exp_f64(p.cmax[bh * T + t] - ms) * p.csum[bh * T + t];
     wt[t] = w;
     part += w;
   }
@@ -713,7 +713,7 @@ __global__ __launch_bounds__(THREADS) void merge_flash_kernel(Problem p) {
     double* pr = p.prob + bh * p.nk;
     for (int64_t n = tid; n < p.nk; n += THREADS) {
       const int t = (int)(n / CHUNK);
-      pr[n] = pr[n] * exp(p.cmax[bh * T + t] - ms) / Z;
+      pr[n] = pr[n] * exp_f64(p.cmax[bh * T + t] - ms) / Z;
     }
   }
 }

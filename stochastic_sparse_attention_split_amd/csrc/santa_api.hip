@@ -461,6 +461,8 @@ void santa_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t 
   out[3] = r.x3;
 }
 
+double santa_exp_f64(double x) { return santa::exp_f64(x); }
+
 const char* santa_status_string(int status) {
   switch (status) {
     case SANTA_OK: return "ok";

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(THREADS) void chunk_cdf_kernel(Problem p) {
     double run = 0.0;
     int lp = -1;
     for (int t = t0; t < t1; ++t) {
-      const double f = exp(cm[t] - ms);
+      const double f = exp_f64(cm[t] - ms);
       const double w = cs[t] * f;
       csc[t] = f;
       cdf[t] = run;  // local exclusive prefix, offset below
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(THREADS, MINB) void score_kernel(Problem p) {
       double ex[4], pre[4], run = 0.0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        ex[i] = (4 * lane + i) < len ? exp(s[i] - m) : 0.0;
+        ex[i] = (4 * lane + i) < len ? exp_f64(s[i] - m) : 0.0;
         run += ex[i];
         pre[i] = run;
       }
@@ -706,7 +706,7 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
         double ex[4], pre[4], run = 0.0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          ex[i] = (4 * lane + i) < len ? exp(sv[i] - m) : 0.0;
+          ex[i] = exp_f64(sv[i] - m);  // keys past the end: -inf -> 0
           run += ex[i];
           pre[i] = run;
         }

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(FM_THREADS) void score_fm_kernel(Problem p) {
     double ex[4], pre[4], run = 0.0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ex[i] = (4 * lane + i) < len ? exp(sv[i] - m) : 0.0;
+      ex[i] = (4 * lane + i) < len ? exp_f64(sv[i] - m) : 0.0;
       run += ex[i];
       pre[i] = run;
     }

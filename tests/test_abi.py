@@ -157,6 +157,39 @@ def test_library_philox_matches_oracle(L):
         assert santa.philox4x32_10(c, k) == want
 
 
+def test_library_exp_matches_libm(L):
+    """The kernels' fp64 exponential (run here on the host through the same inline code) against Python's
+    libm exp: within 4 units in the last place for normal results, within 2 denormal steps below them,
+    exactly 1 at 0 and exactly 0 for -inf and below -746."""
+    import math
+
+    import numpy as np
+
+    assert santa.exp_f64(0.0) == 1.0
+    assert santa.exp_f64(-0.0) == 1.0
+    assert santa.exp_f64(-math.inf) == 0.0
+    assert santa.exp_f64(-746.5) == 0.0
+    rng = np.random.default_rng(5)
+    xs = np.concatenate([
+        -np.linspace(0.0, 745.0, 20001),
+        -rng.exponential(1.0, 20000),                    # the bulk of softmax arguments
+        -np.logspace(-300, 2.8, 4000),                   # tiny and large magnitudes
+        -np.log(2.0) * (np.arange(0, 1075) + 0.5),       # reduction boundaries (k + 1/2) ln2
+        [-709.78, -708.4, -745.13, -744.4, -1e-17],
+    ])
+    worst = 0.0
+    for x in xs:
+        x = float(x)
+        got, ref = santa.exp_f64(x), math.exp(x)
+        if ref >= 2.0 ** -1022:
+            err = abs(got - ref) / math.ulp(ref)
+            worst = max(worst, err)
+            assert err <= 4.0, (x, got, ref)
+        else:
+            assert abs(got - ref) <= 2 * 2.0 ** -1074, (x, got, ref)
+    assert worst <= 4.0
+
+
 def test_status_strings_and_version(L):
     assert santa.version().startswith("santa-mi355x")
     for s in range(5):

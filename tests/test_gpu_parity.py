@@ -408,6 +408,24 @@ def test_strat_equals_iid_at_S1_and_determinism():
     assert torch.equal(a, b)
 
 
+def test_stage_timing_leaves_results_unchanged():
+    """Stage timing launches the score kernel with start/stop events attached (hipExtLaunchKernel): the
+    results equal an untimed call's, and the stage times are ordered (score kernel inside the whole)."""
+    log("stage timing: results and ordering, sequence-major and feature-major score passes")
+    dev = torch.device("cuda:0")
+    q, K, V, _ = workloads.make_inputs(1, 8, 2, 128, 6000, dtype="bf16", spikes_per_head=4, rng_seed=41)
+    qd, Kd, Vd = q.to(dev), K.to(dev), V.to(dev)
+    for kfm in (False, True):
+        Kx = santa.feature_major(Kd) if kfm else Kd
+        a = santa.decode(qd, Kx, Vd, 64, "strat", 9, k_feature_major=kfm)
+        b, info = santa.decode(qd, Kx, Vd, 64, "strat", 9, k_feature_major=kfm, stage_ms=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+        st = info["stage_ms"]
+        assert all(x > 0.0 for x in st), st
+        assert st[0] <= st[3] and st[0] + st[1] + st[2] <= st[3] * 1.0001 + 1e-6, st
+
+
 def test_simple_entry_point_matches_ex():
     log("santa_decode vs santa_decode_ex")
     dev = torch.device("cuda:0")
