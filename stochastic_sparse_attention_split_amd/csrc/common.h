@@ -13,6 +13,10 @@ constexpr int CHUNK = 256;
 constexpr int MAX_CHUNKS = 4096;          // nk <= 2^20 per sequence
 constexpr int MAX_GROUP = 8;              // query heads per KV head handled by one score block
 constexpr int FUSED_CDF_MAX_T = 128;  // up to this many chunks the sampling kernel builds the chunk CDF itself
+// Above this many sampling blocks (B * kv_heads * T; 8 per CU) the chunk CDF is built once per head by its
+// own kernel even for T <= FUSED_CDF_MAX_T: every sampling block would otherwise rebuild all T chunk
+// entries of its heads, fp64 work that then outweighs the extra launch.
+constexpr int64_t SEPARATE_CDF_MIN_BLOCKS = 2048;
 
 // ---------------------------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11):
@@ -361,6 +365,7 @@ struct Problem {
   bool fused;            // S²ANTA-flash sampled and gathered inside the streaming score pass
   bool want_unique;      // fill unique[] (the stats path reads it); the fused S²ANTA-flash skips it otherwise
   bool want_idx;         // the caller asked for idx_out (the fused S²ANTA-flash writes idx only then)
+  bool cdf_done;         // the chunk CDF kernel has run: the sampling kernel reads cdf / cscale / lastpos
   uint64_t* bmap;        // [B, Hkv, T, 4, 4] fused S²ANTA-flash: sampled keys of each (chunk, head) as bits
 };
 

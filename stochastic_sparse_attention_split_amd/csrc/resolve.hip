@@ -721,12 +721,14 @@ __global__ __launch_bounds__(THREADS) void merge_flash_kernel(Problem p) {
 template <int D, bool BF16, int GM>
 hipError_t launch_resolve_g(const Problem& p, hipStream_t st) {
   const dim3 grid(p.T, p.Hkv, p.B);
-  if (p.T <= 64)
+  if (p.cdf_done)
+    resolve_kernel<D, BF16, GM, 0><<<grid, THREADS, 0, st>>>(p);
+  else if (p.T <= 64)
     resolve_kernel<D, BF16, GM, 1><<<grid, THREADS, 0, st>>>(p);
   else if (p.T <= FUSED_CDF_MAX_T)
     resolve_kernel<D, BF16, GM, 2><<<grid, THREADS, 0, st>>>(p);
   else
-    resolve_kernel<D, BF16, GM, 0><<<grid, THREADS, 0, st>>>(p);
+    return hipErrorInvalidValue;  // T > FUSED_CDF_MAX_T always runs the chunk CDF kernel first
   return hipGetLastError();
 }
 

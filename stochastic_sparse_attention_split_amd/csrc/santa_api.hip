@@ -272,7 +272,10 @@ int santa_decode_ex(const santa_args* a) {
   const bool prop = p.mode == SANTA_PROP;
   // for T <= FUSED_CDF_MAX_T the sampling kernel builds the chunk CDF (or the prop tile budgets) itself;
   // S²ANTA-flash needs neither
-  const bool cdf_kernel = p.T > FUSED_CDF_MAX_T && p.mode != SANTA_FLASH;
+  const bool cdf_kernel = p.mode != SANTA_FLASH &&
+                          (p.T > FUSED_CDF_MAX_T ||
+                           (!prop && (int64_t)p.B * p.Hkv * p.T > SEPARATE_CDF_MIN_BLOCKS));
+  p.cdf_done = cdf_kernel && !prop;
   if (cdf_kernel && !prop && (e = launch_chunk_cdf(p, stream)) != hipSuccess)
     return hip_fail(e, "chunk CDF kernel launch");
   if (cdf_kernel && prop && (e = launch_budget(p, stream)) != hipSuccess) return hip_fail(e, "budget kernel launch");
