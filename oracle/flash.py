@@ -38,17 +38,17 @@ TILE = 256
 
 
 def tile_budget(S: int, T: int) -> int:
-    """Algorithm 6, line 1: the uniform per-tile budget S_tile ~ S / T, rounded half up, at least 1."""
+    """Algorithm 6, its budget step: the uniform per-tile budget S_tile ~ S / T, rounded half up, at least 1."""
     return max(1, (2 * S + T) // (2 * T))
 
 
 def offsets(seed: int, b: int, h: int, T: int) -> np.ndarray:
-    """a0_{h,t} ~ U(0,1) per tile (Algorithm 7, line 7), from Philox counter (t, h, b, 4)."""
+    """a0_{h,t} ~ U(0,1) per tile (Algorithm 7, the tile's random offset), from Philox counter (t, h, b, 4)."""
     return np.asarray(philox.uniforms(seed, np.arange(T, dtype=np.int64), h, b, TAG_FLASH), dtype=np.float64)
 
 
 def merge_weights(m: np.ndarray, l: np.ndarray):
-    """Algorithm 8, lines 2-3: W_t = exp(m_t - m*) l_t and Z = sum_t W_t (in tile order)."""
+    """Algorithm 8, its reweighting step: W_t = exp(m_t - m*) l_t and Z = sum_t W_t (in tile order)."""
     m = np.asarray(m, dtype=np.float64)
     l = np.asarray(l, dtype=np.float64)
     W = np.exp(m - float(np.max(m))) * l

@@ -82,7 +82,7 @@ def budgets(m: np.ndarray, l: np.ndarray, S: int):
 
 
 def tile_counts(u: np.ndarray, l_t: float, S_t: int, a0: float):
-    """Algorithm 5, lines 5-9: systematic counts of one tile's keys for budget S_t and offset a0.
+    """Algorithm 5, its counting step: systematic counts of one tile's keys for budget S_t and offset a0.
 
     Returns (c, y): integer counts and the running values y_n = a0 + p after key n (y_{-1} = a0), whose
     distance to the nearest integer tells how close each count was to changing.
@@ -101,7 +101,7 @@ def tile_counts(u: np.ndarray, l_t: float, S_t: int, a0: float):
 
 
 def offsets(seed: int, b: int, h: int, T: int) -> np.ndarray:
-    """a0_{h,t} ~ U(0,1) per tile (Algorithm 4, line 6), from Philox counter (t, h, b, 3)."""
+    """a0_{h,t} ~ U(0,1) per tile (Algorithm 4, the tile's random offset), from Philox counter (t, h, b, 3)."""
     return np.asarray(philox.uniforms(seed, np.arange(T, dtype=np.int64), h, b, TAG_PROP), dtype=np.float64)
 
 

@@ -63,7 +63,7 @@ __device__ inline int last_positive(const double* P, int len) {
 
 // Compaction of the keys counted in `cnt` (16-bit per-head counts, thread k owns key k), gather of their
 // V rows (each row once for the whole group, count * V into fp32 accumulators), and the chunk's partial
-// sums per head (App. O, Algorithm 5, lines 11-14). Ends with every thread past a barrier; `Pt` is reused
+// sums per head (App. O, Algorithm 5, its value-accumulation step). Ends with every thread past a barrier; `Pt` is reused
 // for the cross-wave sums.
 template <int D, bool BF16, int GM>
 __device__ inline void chunk_gather(const Problem& p, int t, int kv, int b, int len, uint32_t* cnt,
