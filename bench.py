@@ -13,6 +13,7 @@ protocol of the paper's kernel benchmark (Appendix Q). Reported alongside:
     recorded at the kernel's own start and end on the launching stream, which gives the roofline of the
     dominant kernel (the score pass: algorithmic bytes = K + q per launch), and the later stages from
     events between the launches;
+  * the same step captured into a HIP graph and replayed (same protocol);
   * the fp64 oracle timed on the host's cores on the same inputs (a baseline, not the target).
 
 Prints one JSON line. --gpus N > 1 is refused: the benchmark runs on one GPU.
@@ -172,6 +173,21 @@ def main():
     us = timed(step, args.steps, cold=True)
     us_warm = timed(step, args.steps, cold=False)
 
+    # the same step captured once into a HIP graph and replayed (the library allocates, synchronises and
+    # clears nothing on this path, so the capture holds exactly its kernel launches)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        santa.decode(q, K, V, w.S, w.mode, w.seed, ternary=ternary, out=out, workspace=ws)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        santa.decode(q, K, V, w.S, w.mode, w.seed, ternary=ternary, out=out, workspace=ws)
+    for _ in range(args.warmup):
+        graph.replay()
+    us_graph = timed(graph.replay, args.steps, cold=True)
+
     # per-kernel times from events between the launches (separate pass, same protocol)
     stage = []
     for _ in range(args.steps):
@@ -302,6 +318,7 @@ def main():
         "us_mean": round(mean, 3),
         "us_min": round(min(us), 3),
         "us_warm_median": round(statistics.median(us_warm), 3),
+        "us_graph_replay_median": round(statistics.median(us_graph), 3),
         "stage_us_mean": {"score": round(score_us, 3), "cdf_resolve": round(float(np.mean(stage[:, 1])), 3),
                           "merge": round(float(np.mean(stage[:, 2])), 3),
                           "total_with_events": round(float(np.mean(stage[:, 3])), 3)},

@@ -426,6 +426,41 @@ def test_stage_timing_leaves_results_unchanged():
         assert st[0] <= st[3] and st[0] + st[1] + st[2] <= st[3] * 1.0001 + 1e-6, st
 
 
+def test_decode_replays_from_a_hip_graph():
+    """santa_decode_ex allocates nothing, synchronises nothing and clears nothing with memset on its default
+    path, so one decode can be captured into a HIP graph: every replay, with eager work and
+    synchronisations between them, equals the eager result bit for bit (sequence-major and feature-major K)."""
+    log("HIP graph capture and replay of one decode step")
+    dev = torch.device("cuda:0")
+    q, K, V, _ = workloads.make_inputs(2, 8, 2, 128, 7000, dtype="bf16", spikes_per_head=4, rng_seed=43)
+    qd, Kd, Vd = q.to(dev), K.to(dev), V.to(dev)
+    for mode, S, kfm in (("strat", 256, False), ("sys", 64, False), ("prop", 128, False), ("flash", 512, False),
+                         ("strat", 128, True)):
+        Kx = santa.feature_major(Kd) if kfm else Kd
+        code = santa.MODES[mode] | (santa.K_FEATURE_MAJOR if kfm else 0)
+        ws = santa.new_workspace(int(santa.lib().santa_workspace_bytes(2, 7000, 8, 2, 128, S, code)), dev)
+        ref = santa.decode(qd, Kx, Vd, S, mode, 11, workspace=ws, k_feature_major=kfm)
+        out = torch.empty_like(ref)
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):  # a call on the capture stream before capturing
+            santa.decode(qd, Kx, Vd, S, mode, 11, out=out, workspace=ws, k_feature_major=kfm)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            santa.decode(qd, Kx, Vd, S, mode, 11, out=out, workspace=ws, k_feature_major=kfm)
+        for r in range(4):
+            out.fill_(float("nan"))
+            junk = torch.randn(1 << 20, device=dev) * r  # eager work between the replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), (mode, S, kfm, r)
+            del junk
+        del g
+
+
 def test_simple_entry_point_matches_ex():
     log("santa_decode vs santa_decode_ex")
     dev = torch.device("cuda:0")
