@@ -474,6 +474,10 @@ __device__ inline bool wait_ge(int* ctr, int target) {
 // dimension and the exponential wave adds the two partial rows. HG = 2 (G = 5..8): the pair splits the
 // heads instead (heads 0-3 and 4-7, each over the whole head dimension), each wave writes complete scores
 // and each exponential wave handles heads w - 8 and w - 4.
+// FD (full rows, G <= 4 without S²ANTA-flash): four matrix waves, one per SIMD, each over its key quarter
+// and the whole head dimension, writing complete scores; the exponential waves are waves 4..7 and the copy
+// waves 8..11 (a 768-thread block). With the K stream writing into LDS, one matrix wave per SIMD over
+// whole rows is no slower than two over half rows, and the partial rows and their addition disappear.
 // FL: S²ANTA-flash kernel 1 ("Stochastic Sparse Attention for Memory-Bound Inference", Section 3.3 and
 // Appendix P, Algorithm 7) fused in: right after a chunk's exponentials, the exponential wave of head g
 // takes the tile's systematic counts with the uniform budget S_tile (c_n = floor(a0 + inv P_n) -
@@ -481,15 +485,18 @@ __device__ inline bool wait_ge(int* ctr, int target) {
 // counter (t, h, b, 4)), writes the index slots and the tile's sampled-key bits, and issues the loads of
 // its sampled V rows; one chunk later (the loads have landed meanwhile) it adds count x row into the fp32
 // tile partial and stores it. Only the merge kernel follows: two launches per decode step.
-template <int D, int HG, bool FL>
-__global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
+template <int D, int HG, bool FL, bool FD = false>
+__global__ __launch_bounds__(64 * ((FD ? SQUART : SMFMA) + SSOFT + SCOPY), 1) void score_stream_kernel(Problem p) {
   static_assert(!FL || HG == 1, "the fused S²ANTA-flash form covers G <= 4");
+  static_assert(!FD || (HG == 1 && !FL), "the full-row form covers G <= 4 without S²ANTA-flash");
+  constexpr int NMF = FD ? SQUART : SMFMA;  // matrix-core waves
+  constexpr int NTH = 64 * (NMF + SSOFT + SCOPY);
   using Sg = SGeo<D>;
   constexpr int EPL = 8, PPH = Sg::PPH, CPW = Sg::CPW;
   constexpr int KPW = CHUNK / SQUART;  // keys per MFMA wave
   constexpr int NGR = KPW / 16;       // 16-key groups per MFMA wave
   constexpr int HM = 4 * HG;          // heads held
-  constexpr int NPW = HG == 1 ? PPH : 2 * PPH;  // 4-piece steps of a row per MFMA wave
+  constexpr int NPW = HG == 1 && !FD ? PPH : 2 * PPH;  // 4-piece steps of a row per MFMA wave
   static_assert(D * 2 * HM <= 1024 * HG, "the queries of a group fit HG 1 KiB copies");
 
   __shared__ __align__(16) unsigned char kt[2][Sg::TILE];
@@ -532,17 +539,17 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
     if (lane == 0) {
       if (!ok) __hip_atomic_fetch_or(bad, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       const int before = __hip_atomic_fetch_add(fin, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      if (before == STHREADS / 64 - 1)
+      if (before == NTH / 64 - 1)
         __hip_atomic_store(err, __hip_atomic_load(bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
 
-  if (wave >= SMFMA + SSOFT) {
+  if (wave >= NMF + SSOFT) {
     // ---- copy waves: at most one chunk's copies in flight per wave, so vmcnt(0) means all landed.
     // Highest issue priority on their SIMD: they issue rarely and the whole block waits on them.
     __builtin_amdgcn_s_setprio(3);
-    const int j = (wave - SMFMA - SSOFT) >> 1, hf = (wave - SMFMA - SSOFT) & 1;
+    const int j = (wave - NMF - SSOFT) >> 1, hf = (wave - NMF - SSOFT) & 1;
     if (j == 1 && hf == 0) {
       const char* qsrc = (const char*)p.q + ((int64_t)b * p.H + h0) * D * 2;
 #pragma unroll
@@ -552,7 +559,7 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
       signal(qr, lane);
     }
     for (int k = j, m = 0; k < n && ok; k += 2, ++m) {
-      if (m > 0) ok = wait_ge(&use[j], SMFMA * m);  // the tile's previous chunk is no longer read
+      if (m > 0) ok = wait_ge(&use[j], NMF * m);  // the tile's previous chunk is no longer read
       if (m == 0 && j == 1) ok = wait_ge(&ld[0], 2);  // the block's first chunk goes first
       if (!ok) break;
       const int t = t0 + k * step;
@@ -580,11 +587,11 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   auto pbar = [&]() {
     signal(pb, lane);
     ++np;
-    ok = ok && wait_ge(pb, (SMFMA + SSOFT) * np);
+    ok = ok && wait_ge(pb, (NMF + SSOFT) * np);
   };
   ok = wait_ge(qr, 1);
   if (ok) {
-    for (int i = tid; i < HM * D; i += (SMFMA + SSOFT) * 64) {
+    for (int i = tid; i < HM * D; i += (NMF + SSOFT) * 64) {
       const int g = i / D, e = i % D;
       double v = 0.0;
       if (g < G) v = (double)__uint_as_float(((uint32_t)((const uint16_t*)qs)[g * D + e]) << 16);
@@ -600,7 +607,7 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
     }
     pbar();
     if (ok) {
-      for (int i = tid; i < HM * D; i += (SMFMA + SSOFT) * 64) {
+      for (int i = tid; i < HM * D; i += (NMF + SSOFT) * 64) {
         const int g = i / D, e = i % D;
         const double v = qe[g][e];
         const double nrm = hnorm[g];
@@ -615,11 +622,11 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
     pbar();
   }
 
-  if (wave >= SMFMA) {
+  if (wave >= NMF) {
     // ---- exponential waves: heads w - 8 (+ 4) of every chunk, lane owns keys 4*lane .. 4*lane + 3. Issue
     // priority above the MFMA waves sharing their SIMD, whose instruction stream would otherwise starve them.
     __builtin_amdgcn_s_setprio(2);
-    const int g0 = wave - SMFMA;
+    const int g0 = wave - NMF;
     // fused S²ANTA-flash state: V-row loads of the previous chunk still in flight
     constexpr int LPR = D / 8;     // lanes per V row (16-byte pieces)
     constexpr int RPI = 64 / LPR;  // rows per load instruction
@@ -660,14 +667,14 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
       tpend = -1;
     };
     for (int k = 0; k < n && ok; ++k) {
-      ok = wait_ge(pr, SMFMA * (k + 1));  // chunk k's partials are complete
+      ok = wait_ge(pr, NMF * (k + 1));  // chunk k's partials are complete
       if (!ok) break;
       double raw[HG][4];
 #pragma unroll
       for (int hx = 0; hx < HG; ++hx) {
         const double2* lo = (const double2*)&part[HG == 1 ? 0 : hx][g0][4 * lane];
         const double2 l0 = lo[0], l1 = lo[1];
-        if constexpr (HG == 1) {  // lower + upper half of the head dimension
+        if constexpr (HG == 1 && !FD) {  // lower + upper half of the head dimension
           const double2* hi = (const double2*)&part[1][g0][4 * lane];
           const double2 h0v = hi[0], h1v = hi[1];
           raw[hx][0] = l0.x + h0v.x;
@@ -826,8 +833,8 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   // ---- MFMA waves: 16-key groups x element parity = independent accumulation chains
   const int slot = lane >> 4;
   // key quarter; half of the head dimension (HG = 1) or head group (HG = 2)
-  const int quart = wave & (SQUART - 1), dh = wave / SQUART;
-  const int pbase = HG == 1 ? dh * PPH : 0;         // first 4-piece step of this wave's part of a row
+  const int quart = FD ? wave : wave & (SQUART - 1), dh = FD ? 0 : wave / SQUART;
+  const int pbase = HG == 1 && !FD ? dh * PPH : 0;  // first 4-piece step of this wave's part of a row
   const int qrow = HG == 1 ? (lane & 3) : 4 * dh + (lane & 3);
   double qb[NPW][EPL];
 #pragma unroll
@@ -886,7 +893,8 @@ hipError_t launch_d(const Problem& p, hipStream_t st, const LaunchEvents& ev) {
     const dim3 grid(p.score_blocks_per_group, p.Hkv, p.B);
     if (p.G <= 4) {
       if (p.fused) return launch_timed(score_stream_kernel<D, 1, true>, grid, dim3(STHREADS), st, ev, p);
-      return launch_timed(score_stream_kernel<D, 1, false>, grid, dim3(STHREADS), st, ev, p);
+      return launch_timed(score_stream_kernel<D, 1, false, true>, grid, dim3(64 * (SQUART + SSOFT + SCOPY)), st, ev,
+                          p);
     }
     return launch_timed(score_stream_kernel<D, 2, false>, grid, dim3(STHREADS), st, ev, p);
   }
