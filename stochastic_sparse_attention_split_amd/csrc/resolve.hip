@@ -68,13 +68,15 @@ __device__ inline int last_positive(const double* P, int len) {
 template <int D, bool BF16, int GM>
 __device__ inline void chunk_gather(const Problem& p, int t, int kv, int b, int len, uint32_t* cnt,
                                     int32_t* lkey, uint32_t (*lcnt)[GM / 2], int* wsum_i, double (*Pt)[CHUNK]) {
-  using Pc = Piece<BF16>;
-  constexpr int EPL = Pc::EPL;
+  // 4 elements per lane (8 bytes of bf16 or 16 of fp32): the per-head accumulators stay small enough for
+  // eight resident blocks per CU, which large grids need more than wide loads for a handful of rows
+  constexpr int EPL = 4;
   constexpr int LPR = D / EPL;          // lanes per V row
   constexpr int NRG = THREADS / LPR;    // row groups
   constexpr int NWAVE = THREADS / 64;
   constexpr int NCW = GM / 2;
   constexpr int CW = NCW + 1;
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = p.G, T = p.T;
   const int grp = b * p.Hkv + kv;
@@ -133,13 +135,26 @@ __device__ inline void chunk_gather(const Problem& p, int t, int kv, int b, int 
 #pragma unroll
       for (int w = 0; w < NCW; ++w) cw[k][w] = u < nu ? lcnt[uu][w] : 0u;
     }
-    uint4 w4[BATCH];
+    float vv[BATCH][EPL];
+    if constexpr (BF16) {
+      u32x2_t w2[BATCH];
 #pragma unroll
-    for (int k = 0; k < BATCH; ++k) w4[k] = load_stream16((const uint4*)(vbase + key[k] * rstride) + pc);
+      for (int k = 0; k < BATCH; ++k)
+        w2[k] = __builtin_nontemporal_load((const u32x2_t*)(vbase + key[k] * rstride) + pc);
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) {
+        vv[k][0] = bf16_lo(w2[k].x);
+        vv[k][1] = bf16_hi(w2[k].x);
+        vv[k][2] = bf16_lo(w2[k].y);
+        vv[k][3] = bf16_hi(w2[k].y);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) Piece<false>::to_f32(load_stream16((const uint4*)(vbase + key[k] * rstride) + pc), vv[k]);
+    }
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
-      float v[EPL];
-      Pc::to_f32(w4[k], v);
+      const float* v = vv[k];
 #pragma unroll
       for (int g = 0; g < GM; ++g) {
         const uint32_t c32 = cw[k][g >> 1];
