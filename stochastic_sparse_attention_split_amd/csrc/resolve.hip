@@ -591,12 +591,14 @@ __global__ __launch_bounds__(THREADS) void resolve_prop_kernel(Problem p) {
   chunk_gather<D, BF16, GM>(p, t, kv, b, len, cnt, lkey, lcnt, wsum_i, Pt);
 }
 
-// out[b, h] = round((sum over chunks of the partials of head h) / S); fp64 sum in chunk order
-template <int D, bool BF16>
-__global__ __launch_bounds__(THREADS) void merge_kernel(Problem p) {
+// out[b, h] = round((sum over chunks of the partials of head h) / S). 1024 threads: D / 4 float4 columns x
+// TS chunk slices; slice ts adds chunks ts, ts + TS, ... in fp64 in that order (MB loads in flight per
+// thread, one round for T <= TS * MB), then the slices are added in order: a fixed order for every call.
+constexpr int MTHREADS = 1024;
+template <int D, bool BF16, int MB>
+__global__ __launch_bounds__(MTHREADS) void merge_kernel(Problem p) {
   constexpr int V4 = D / 4;            // float4 pieces per row
-  constexpr int TS = THREADS / V4;     // chunk slices
-  constexpr int MB = 16;               // loads in flight per thread
+  constexpr int TS = MTHREADS / V4;    // chunk slices
   __shared__ double red[TS][D];
   const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
@@ -630,8 +632,8 @@ __global__ __launch_bounds__(THREADS) void merge_kernel(Problem p) {
   __syncthreads();
   if (tid < D) {
     double tot = 0.0;
-#pragma unroll
-    for (int s = 0; s < TS; ++s) tot += red[s][tid];
+#pragma unroll 8
+    for (int s2 = 0; s2 < TS; ++s2) tot += red[s2][tid];
     const double r = tot / (double)p.S;
     const int64_t o = ((int64_t)b * p.H + h) * D + tid;
     if (BF16)
@@ -798,12 +800,24 @@ hipError_t launch_merge(const Problem& p, hipStream_t st) {
     }
     return hipGetLastError();
   }
+  // loads in flight per thread: one round for up to 128 chunks (d = 128: 32 slices x 4), else 16 per round
+  const bool small = p.T <= MTHREADS / 32 * 4;
   if (p.d == 128) {
-    if (p.bf16) merge_kernel<128, true><<<grid, THREADS, 0, st>>>(p);
-    else merge_kernel<128, false><<<grid, THREADS, 0, st>>>(p);
+    if (small) {
+      if (p.bf16) merge_kernel<128, true, 4><<<grid, MTHREADS, 0, st>>>(p);
+      else merge_kernel<128, false, 4><<<grid, MTHREADS, 0, st>>>(p);
+    } else {
+      if (p.bf16) merge_kernel<128, true, 16><<<grid, MTHREADS, 0, st>>>(p);
+      else merge_kernel<128, false, 16><<<grid, MTHREADS, 0, st>>>(p);
+    }
   } else {
-    if (p.bf16) merge_kernel<64, true><<<grid, THREADS, 0, st>>>(p);
-    else merge_kernel<64, false><<<grid, THREADS, 0, st>>>(p);
+    if (small) {
+      if (p.bf16) merge_kernel<64, true, 4><<<grid, MTHREADS, 0, st>>>(p);
+      else merge_kernel<64, false, 4><<<grid, MTHREADS, 0, st>>>(p);
+    } else {
+      if (p.bf16) merge_kernel<64, true, 16><<<grid, MTHREADS, 0, st>>>(p);
+      else merge_kernel<64, false, 16><<<grid, MTHREADS, 0, st>>>(p);
+    }
   }
   return hipGetLastError();
 }
