@@ -230,7 +230,10 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
   const int64_t rstride = esz * p.seq_stride;
 
   // ---- every load of the sampling phase at once (heads clamped to G - 1 and keys to the chunk's last
-  //      key, so every address is valid): this wave's prefix rows and its heads' chunk CDF inputs
+  //      key, so every address is valid): this wave's heads' chunk CDF inputs first, then its prefix rows.
+  //      Loads complete in issue order as far as the wait counter is concerned, so the chunk CDF can be
+  //      built as soon as its few inputs have landed, while the prefix rows (the bulk of the bytes every
+  //      block requests at once) are still in flight.
   double pv[HPW][4];
   double cm[HPW][PERL], cl[HPW][PERL];
   double e0[HPW], e1[HPW], eZ[HPW], eF[HPW];
@@ -238,8 +241,6 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     const int64_t bh = bh0 + min(wave + NWAVE * hh, G - 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pv[hh][i] = p.stash[bh * p.stash_stride + n0 + min(4 * lane + i, len - 1)];
     if constexpr (PER > 0) {
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
@@ -255,6 +256,13 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
       eF[hh] = p.cscale[bh * T + t];
       eL[hh] = p.lastpos[bh];
     }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the prefix-row loads behind the statistics loads
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int64_t bh = bh0 + min(wave + NWAVE * hh, G - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[hh][i] = p.stash[bh * p.stash_stride + n0 + min(4 * lane + i, len - 1)];
   }
   for (int i = tid; i < CHUNK * CW; i += THREADS) cnt[i] = 0u;
   __syncthreads();  // counters zeroed before any wave counts (does not wait for the loads above)
