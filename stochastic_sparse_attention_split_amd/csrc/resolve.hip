@@ -505,14 +505,14 @@ __global__ __launch_bounds__(THREADS) void resolve_prop_kernel(Problem p) {
   const int64_t n0 = (int64_t)t * CHUNK;
   const int len = (int)min((int64_t)CHUNK, p.nk - n0);
 
-  // every load at once (heads clamped to G - 1, keys to the chunk's last key, tiles to T - 1)
+  // every load at once (heads clamped to G - 1, keys to the chunk's last key, tiles to T - 1): the tile
+  // statistics and budgets first, the prefix rows (the bulk of the bytes) last, so that the budgets can
+  // be formed while the prefix rows are still in flight (wait counters retire loads in issue order)
   double pv[HPW][4];
   double cm[HPW][PL], cl[HPW][PL];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     const int64_t bh = bh0 + min(wave + NWAVE * hh, G - 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pv[hh][i] = p.stash[bh * p.stash_stride + n0 + min(4 * lane + i, len - 1)];
     if constexpr (PER > 0) {
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
@@ -535,13 +535,16 @@ __global__ __launch_bounds__(THREADS) void resolve_prop_kernel(Problem p) {
     f = p.cscale[bhg * T + t];
     Z = p.cdf[bhg * (T + 1) + T];
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep the prefix-row loads behind the statistics loads
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int64_t bh = bh0 + min(wave + NWAVE * hh, G - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[hh][i] = p.stash[bh * p.stash_stride + n0 + min(4 * lane + i, len - 1)];
+  }
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     const int g = wave + NWAVE * hh;
-    if (g < GM) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Pt[g][4 * lane + i] = pv[hh][i];
-    }
     if constexpr (PER > 0) {
       if (g < G) {
         const TileBudget r = tile_budget_wave<PER>(cm[hh], cl[hh], T, S, t, lane, hist[wave]);
@@ -552,6 +555,14 @@ __global__ __launch_bounds__(THREADS) void resolve_prop_kernel(Problem p) {
           hZ[g] = r.Z;
         }
       }
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int g = wave + NWAVE * hh;
+    if (g < GM) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Pt[g][4 * lane + i] = pv[hh][i];
     }
   }
   if (tid < G) {
