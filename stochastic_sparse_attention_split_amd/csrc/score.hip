@@ -721,11 +721,16 @@ __global__ __launch_bounds__(64 * ((FD ? SQUART : SMFMA) + SSOFT + SCOPY), 1) vo
         double excl = __shfl_up(incl, 1, 64);
         if (lane == 0) excl = 0.0;
         // stash rows are CHUNK-padded: the whole chunk is stored, keys past the end repeat the total (the
-        // fused S²ANTA-flash samples here and needs no stash)
+        // fused S²ANTA-flash samples here and needs no stash). Non-temporal stores: the rows leave the
+        // caches as they are written instead of as dirty lines written back at the end of the kernel; the
+        // sampling kernel reads them only after its chunk CDF and points.
         if constexpr (!FL) {
-          double2* dst = (double2*)(p.stash + bh * p.stash_stride + n0 + 4 * lane);
-          dst[0] = make_double2(excl + pre[0], excl + pre[1]);
-          dst[1] = make_double2(excl + pre[2], excl + pre[3]);
+          typedef double f64x2_t __attribute__((ext_vector_type(2)));
+          f64x2_t* dst = (f64x2_t*)(p.stash + bh * p.stash_stride + n0 + 4 * lane);
+          const f64x2_t v0 = {excl + pre[0], excl + pre[1]};
+          const f64x2_t v1 = {excl + pre[2], excl + pre[3]};
+          __builtin_nontemporal_store(v0, dst);
+          __builtin_nontemporal_store(v1, dst + 1);
         }
         if (lane == 0) {
           p.cmax[bh * T + t] = m;
