@@ -450,9 +450,10 @@ __device__ inline bool wait_ge(int* ctr, int target) {
   return true;
 }
 
-// Streaming score pass for bf16 caches and G <= 8, one block of 16 waves per CU, three roles that meet
-// only through LDS counters (no block-wide barrier after the start), so the K stream, the matrix cores
-// and the exponentials overlap:
+// Streaming score pass for bf16 caches and G <= 8, one block per CU, three roles that meet only through
+// LDS counters (no block-wide barrier after the start), so the K stream, the matrix cores and the
+// exponentials overlap. The 16-wave layout below serves the fused S²ANTA-flash pass; every other call
+// runs the 12-wave full-row form (FD, further down) with the same exponential and copy roles:
 //   * waves 0..7 (two per SIMD): fp64 MFMA over key quarter w & 3 (64 keys: four 16-key groups) and
 //     half w >> 2 of the head dimension (element parity gives eight independent accumulation chains per
 //     wave); each writes its partial dot products into the partial row of its half. Two waves per SIMD
@@ -470,14 +471,16 @@ __device__ inline bool wait_ge(int* ctr, int target) {
 //   partials are written;  pc +1 per exponential wave per chunk whose partials it has read;  qr queries
 //   landed;  pb prologue barrier;  fin waves finished (the last one publishes the block's handshake
 //   status).
-// HG = head groups of four (G <= 4 * HG). HG = 1: the MFMA wave pair of a key quarter splits the head
-// dimension and the exponential wave adds the two partial rows. HG = 2 (G = 5..8): the pair splits the
-// heads instead (heads 0-3 and 4-7, each over the whole head dimension), each wave writes complete scores
-// and each exponential wave handles heads w - 8 and w - 4.
-// FD (full rows, G <= 4 without S²ANTA-flash): four matrix waves, one per SIMD, each over its key quarter
+// HG = head groups of four (G <= 4 * HG). Without FD (the fused S²ANTA-flash pass, G <= 4) the MFMA wave
+// pair of a key quarter splits the head dimension and the exponential wave adds the two partial rows.
+// With HG = 2 (G = 5..8) each exponential wave handles heads g and g + 4.
+// FD (full rows, without S²ANTA-flash): four matrix waves, one per SIMD, each over its key quarter
 // and the whole head dimension, writing complete scores; the exponential waves are waves 4..7 and the copy
 // waves 8..11 (a 768-thread block). With the K stream writing into LDS, one matrix wave per SIMD over
 // whole rows is no slower than two over half rows, and the partial rows and their addition disappear.
+// With HG = 2 the wave scores both head groups: each K element is converted once for the MFMAs of the
+// eight heads (the query operands are read from LDS per 4-piece step to stay within the register budget
+// of three waves per SIMD), and its sums run in the same order as the HG = 2 pair's.
 // FL: S²ANTA-flash kernel 1 ("Stochastic Sparse Attention for Memory-Bound Inference", Section 3.3 and
 // Appendix P, Algorithm 7) fused in: right after a chunk's exponentials, the exponential wave of head g
 // takes the tile's systematic counts with the uniform budget S_tile (c_n = floor(a0 + inv P_n) -
@@ -488,7 +491,8 @@ __device__ inline bool wait_ge(int* ctr, int target) {
 template <int D, int HG, bool FL, bool FD = false>
 __global__ __launch_bounds__(64 * ((FD ? SQUART : SMFMA) + SSOFT + SCOPY), 1) void score_stream_kernel(Problem p) {
   static_assert(!FL || HG == 1, "the fused S²ANTA-flash form covers G <= 4");
-  static_assert(!FD || (HG == 1 && !FL), "the full-row form covers G <= 4 without S²ANTA-flash");
+  static_assert(!FD || !FL, "the full-row form does not take the fused S²ANTA-flash pass");
+  static_assert(FD || HG == 1, "G = 5..8 runs in the full-row form");
   constexpr int NMF = FD ? SQUART : SMFMA;  // matrix-core waves
   constexpr int NTH = 64 * (NMF + SSOFT + SCOPY);
   using Sg = SGeo<D>;
@@ -837,6 +841,53 @@ __global__ __launch_bounds__(64 * ((FD ? SQUART : SMFMA) + SSOFT + SCOPY), 1) vo
 
   // ---- MFMA waves: 16-key groups x element parity = independent accumulation chains
   const int slot = lane >> 4;
+  if constexpr (FD && HG == 2) {
+    const int quart = wave;
+    for (int k = 0; k < n && ok; ++k) {
+      ok = wait_ge(&ld[k & 1], 2 * ((k >> 1) + 1));  // chunk k's tile has landed
+      if (!ok) break;
+      const unsigned char* ks = &kt[k & 1][0];
+      double acc[HG][NGR][2];  // [head group][key group][element parity]
+#pragma unroll
+      for (int hx = 0; hx < HG; ++hx)
+#pragma unroll
+        for (int gi = 0; gi < NGR; ++gi) acc[hx][gi][0] = acc[hx][gi][1] = 0.0;
+#pragma unroll
+      for (int pp = 0; pp < NPW; ++pp) {
+        uint4 a4[NGR];
+#pragma unroll
+        for (int gi = 0; gi < NGR; ++gi)
+          a4[gi] = *(const uint4*)(ks + tile_off<D>(quart * KPW + gi * 16 + (lane & 15), 4 * pp + slot));
+        double qv[HG][EPL];
+#pragma unroll
+        for (int hx = 0; hx < HG; ++hx)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) qv[hx][e] = qe[4 * hx + (lane & 3)][EPL * (4 * pp + slot) + e];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+#pragma unroll
+          for (int gi = 0; gi < NGR; ++gi) {
+            const double a = piece_elem<true>(a4[gi], e);
+#pragma unroll
+            for (int hx = 0; hx < HG; ++hx)
+              acc[hx][gi][e & 1] = __builtin_amdgcn_mfma_f64_4x4x4f64(a, qv[hx][e], acc[hx][gi][e & 1], 0, 0, 0);
+          }
+      }
+      signal(&use[k & 1], lane);  // this wave's reads of tile k & 1 are complete
+      if (k >= 1) ok = wait_ge(pc, SSOFT * k);  // chunk k - 1's partials were read
+      if (!ok) break;
+#pragma unroll
+      for (int hx = 0; hx < HG; ++hx)
+#pragma unroll
+        for (int gi = 0; gi < NGR; ++gi) {
+          const int key = quart * KPW + gi * 16 + 4 * ((lane >> 2) & 3) + (lane >> 4);
+          part[hx][lane & 3][key] = acc[hx][gi][0] + acc[hx][gi][1];
+        }
+      signal(pr, lane);
+    }
+    finish();
+    return;
+  }
   // key quarter; half of the head dimension (HG = 1) or head group (HG = 2)
   const int quart = FD ? wave : wave & (SQUART - 1), dh = FD ? 0 : wave / SQUART;
   const int pbase = HG == 1 && !FD ? dh * PPH : 0;  // first 4-piece step of this wave's part of a row
@@ -901,7 +952,8 @@ hipError_t launch_d(const Problem& p, hipStream_t st, const LaunchEvents& ev) {
       return launch_timed(score_stream_kernel<D, 1, false, true>, grid, dim3(64 * (SQUART + SSOFT + SCOPY)), st, ev,
                           p);
     }
-    return launch_timed(score_stream_kernel<D, 2, false>, grid, dim3(STHREADS), st, ev, p);
+    return launch_timed(score_stream_kernel<D, 2, false, true>, grid, dim3(64 * (SQUART + SSOFT + SCOPY)), st, ev,
+                        p);
   }
   return p.G <= 4 ? launch_q<D, BF16, 1>(p, st, ev) : launch_q<D, BF16, 2>(p, st, ev);
 }
