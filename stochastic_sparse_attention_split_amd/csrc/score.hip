@@ -86,21 +86,19 @@ __device__ inline void store_rows(unsigned char* ks, const uint4* r, int tid) {
 }
 
 // Chunk CDF (Appendix O, Algorithm 4: m* = max_t m_t, W_t = l_t exp(m_t - m*), Z = sum_t W_t) of the
-// heads of one (KV head, sequence) group, one wave per head (waves take heads wave, wave + 4): lane l owns
-// a contiguous run of chunks; the prefix is exclusive, then made monotone by a running maximum so that
-// the chunks' intervals [cdf_t, cdf_{t+1}) partition [0, Z) exactly. cdf[T] = Z. One block per group.
+// one (query head, sequence) per one-wave block, so every head's CDF is built at once: lane l owns a
+// contiguous run of chunks; the prefix is exclusive, then made monotone by a running maximum so that
+// the chunks' intervals [cdf_t, cdf_{t+1}) partition [0, Z) exactly. cdf[T] = Z.
 // Register form: T <= 64 * PER and lane l owns chunks [l*PER, l*PER + PER), held in registers, so the statistics
 // are read in one round trip. The plain form below takes any T: lane l owns a contiguous run of ceil(T/64)
 // chunks, re-read from memory between the steps.
 template <int PER>
-__global__ __launch_bounds__(THREADS) void chunk_cdf_reg_kernel(Problem p) {
-  const int kv = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h0 = kv * p.G;
+__global__ __launch_bounds__(64) void chunk_cdf_reg_kernel(Problem p) {
+  const int lane = threadIdx.x;
   const int T = p.T;
   const int t0 = lane * PER;
-  for (int g = wave; g < p.G; g += THREADS / 64) {
-    const int64_t bh = (int64_t)b * p.H + h0 + g;
+  {
+    const int64_t bh = (int64_t)blockIdx.y * p.H + blockIdx.x;
     double m[PER], l[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
@@ -126,15 +124,13 @@ __global__ __launch_bounds__(THREADS) void chunk_cdf_reg_kernel(Problem p) {
   }
 }
 
-__global__ __launch_bounds__(THREADS) void chunk_cdf_kernel(Problem p) {
-  const int kv = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h0 = kv * p.G;
+__global__ __launch_bounds__(64) void chunk_cdf_kernel(Problem p) {
+  const int lane = threadIdx.x;
   const int T = p.T;
   const int per = (T + 63) / 64;
   const int t0 = min(T, lane * per), t1 = min(T, t0 + per);
-  for (int g = wave; g < p.G; g += THREADS / 64) {
-    const int64_t bh = (int64_t)b * p.H + h0 + g;
+  {
+    const int64_t bh = (int64_t)blockIdx.y * p.H + blockIdx.x;
     const double* cm = p.cmax + bh * T;
     const double* cs = p.csum + bh * T;
     double* cdf = p.cdf + bh * (T + 1);
@@ -977,19 +973,19 @@ hipError_t launch_score(const Problem& p, hipStream_t st, const LaunchEvents& ev
 }
 
 hipError_t launch_chunk_cdf(const Problem& p, hipStream_t st) {
-  const dim3 grid(p.Hkv, p.B);
+  const dim3 grid(p.H, p.B);  // one wave per (query head, sequence)
   if (p.T <= 64)
-    chunk_cdf_reg_kernel<1><<<grid, THREADS, 0, st>>>(p);
+    chunk_cdf_reg_kernel<1><<<grid, 64, 0, st>>>(p);
   else if (p.T <= 128)
-    chunk_cdf_reg_kernel<2><<<grid, THREADS, 0, st>>>(p);
+    chunk_cdf_reg_kernel<2><<<grid, 64, 0, st>>>(p);
   else if (p.T <= 256)
-    chunk_cdf_reg_kernel<4><<<grid, THREADS, 0, st>>>(p);
+    chunk_cdf_reg_kernel<4><<<grid, 64, 0, st>>>(p);
   else if (p.T <= 512)
-    chunk_cdf_reg_kernel<8><<<grid, THREADS, 0, st>>>(p);
+    chunk_cdf_reg_kernel<8><<<grid, 64, 0, st>>>(p);
   else if (p.T <= 1024)
-    chunk_cdf_reg_kernel<16><<<grid, THREADS, 0, st>>>(p);
+    chunk_cdf_reg_kernel<16><<<grid, 64, 0, st>>>(p);
   else
-    chunk_cdf_kernel<<<grid, THREADS, 0, st>>>(p);
+    chunk_cdf_kernel<<<grid, 64, 0, st>>>(p);
   return hipGetLastError();
 }
 
