@@ -229,8 +229,10 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
   const char* vbase = (const char*)p.V + esz * ((int64_t)b * p.batch_stride + n0 * p.seq_stride + (int64_t)kv * D);
   const int64_t rstride = esz * p.seq_stride;
 
-  // ---- every load of the sampling phase at once (heads clamped to G - 1 and keys to the chunk's last
-  //      key, so every address is valid): this wave's heads' chunk CDF inputs first, then its prefix rows.
+  // ---- the loads of the sampling phase (heads clamped to G - 1 and keys to the chunk's last key, so every
+  //      address is valid): this wave's heads' chunk CDF inputs first, then, when the chunk CDF is built
+  //      here, its prefix rows at once (with a precomputed chunk CDF they are read per head once a point
+  //      is known to fall in the chunk).
   //      Loads complete in issue order as far as the wait counter is concerned, so the chunk CDF can be
   //      built as soon as its few inputs have landed, while the prefix rows (the bulk of the bytes every
   //      block requests at once) are still in flight.
@@ -258,11 +260,13 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the prefix-row loads behind the statistics loads
+  if constexpr (PER > 0) {
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    const int64_t bh = bh0 + min(wave + NWAVE * hh, G - 1);
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int64_t bh = bh0 + min(wave + NWAVE * hh, G - 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pv[hh][i] = p.stash[bh * p.stash_stride + n0 + min(4 * lane + i, len - 1)];
+      for (int i = 0; i < 4; ++i) pv[hh][i] = p.stash[bh * p.stash_stride + n0 + min(4 * lane + i, len - 1)];
+    }
   }
   for (int i = tid; i < CHUNK * CW; i += THREADS) cnt[i] = 0u;
   __syncthreads();  // counters zeroed before any wave counts (does not wait for the loads above)
@@ -292,11 +296,13 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
       lastc = eL[hh];
     }
     // this head's prefix row, written and then searched by this wave only
+    if constexpr (PER > 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Pt[g][4 * lane + i] = pv[hh][i];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int i = 0; i < 4; ++i) Pt[g][4 * lane + i] = pv[hh][i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
 
     if (p.prob) {  // debug: probabilities of this chunk's keys from the score pass's exponentials
       double* pr = p.prob + (bh0 + g) * p.nk + n0;
@@ -314,6 +320,25 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
         lo = ilo;
         n = ihi >= ilo ? ihi - ilo + 1 : 0;
       }
+    }
+    if constexpr (PER <= 0) {
+      // with the chunk CDF known from the start, the prefix row is read only when one of the head's
+      // points falls in this chunk (most chunks hold none): the points are tested first, then found again
+      bool any = false;
+      for (int c = lane; c < n; c += 64) {
+        const double y = point_of(p, lo + c, h0 + g, b, u_sys) * Z;
+        any = any || (y < Z ? (c0 <= y && y < c1) : (t == lastc));
+      }
+      if (__ballot(any) == 0ull) continue;  // wave-uniform
+      const int64_t bh = bh0 + g;
+      double v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = p.stash[bh * p.stash_stride + n0 + min(4 * lane + i, len - 1)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Pt[g][4 * lane + i] = v[i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     for (int c = lane; c < n; c += 64) {
       const int m = lo + c;
