@@ -635,21 +635,28 @@ __global__ __launch_bounds__(THREADS) void resolve_prop_kernel(Problem p) {
   chunk_gather<D, BF16, GM>(p, t, kv, b, len, cnt, lkey, lcnt, wsum_i, Pt);
 }
 
-// out[b, h] = round((sum over chunks of the partials of head h) / S). 1024 threads: D / 4 float4 columns x
-// TS chunk slices; slice ts adds chunks ts, ts + TS, ... in fp64 in that order (MB loads in flight per
-// thread, one round for T <= TS * MB), then the slices are added in order: a fixed order for every call.
-constexpr int MTHREADS = 1024;
+// out[b, h] = round((sum over chunks of the partials of head h) / S). One block per (head, sequence, group
+// of MCOLS columns of the head dimension), so a head's partials are read by D / MCOLS CUs: MCOLS / 4
+// float4 columns x TS chunk slices (TS = 4096 / D); slice ts adds chunks ts, ts + TS, ... in fp64 in that
+// order (MB loads in flight per thread, one round for T <= TS * MB), then the slices are added in order:
+// a fixed order for every call.
+constexpr int MTHREADS = 1024;  // threads over a whole row: sets the slice count
+constexpr int MCOLS = 32;       // head-dimension columns per block
+template <int D>
+constexpr int merge_slices() { return MTHREADS / (D / 4); }
+template <int D>
+constexpr int merge_threads() { return MCOLS / 4 * merge_slices<D>(); }
 template <int D, bool BF16, int MB>
-__global__ __launch_bounds__(MTHREADS) void merge_kernel(Problem p) {
-  constexpr int V4 = D / 4;            // float4 pieces per row
-  constexpr int TS = MTHREADS / V4;    // chunk slices
-  __shared__ double red[TS][D];
-  const int h = blockIdx.x, b = blockIdx.y;
+__global__ __launch_bounds__(merge_threads<D>()) void merge_kernel(Problem p) {
+  constexpr int V4 = MCOLS / 4;          // float4 pieces per block row
+  constexpr int TS = merge_slices<D>();  // chunk slices
+  __shared__ double red[TS][MCOLS];
+  const int h = blockIdx.x, b = blockIdx.y, col0 = blockIdx.z * MCOLS;
   const int tid = threadIdx.x;
   const int G = p.G, T = p.T;
   const int kv = h / G, g = h % G;
   const int c = tid % V4, ts = tid / V4;
-  const float* base = p.partial + ((int64_t)(b * p.Hkv + kv) * T * G + g) * D + 4 * c;
+  const float* base = p.partial + ((int64_t)(b * p.Hkv + kv) * T * G + g) * D + col0 + 4 * c;
   const int64_t tstride = (int64_t)G * D;
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
   for (int t0 = ts; t0 < T; t0 += TS * MB) {
@@ -674,12 +681,12 @@ __global__ __launch_bounds__(MTHREADS) void merge_kernel(Problem p) {
   red[ts][4 * c + 2] = a2;
   red[ts][4 * c + 3] = a3;
   __syncthreads();
-  if (tid < D) {
+  if (tid < MCOLS) {
     double tot = 0.0;
 #pragma unroll 8
     for (int s2 = 0; s2 < TS; ++s2) tot += red[s2][tid];
     const double r = tot / (double)p.S;
-    const int64_t o = ((int64_t)b * p.H + h) * D + tid;
+    const int64_t o = ((int64_t)b * p.H + h) * D + col0 + tid;
     if (BF16)
       ((uint16_t*)p.out)[o] = f64_to_bf16_rne(r);
     else
@@ -846,21 +853,24 @@ hipError_t launch_merge(const Problem& p, hipStream_t st) {
   }
   // loads in flight per thread: one round for up to 128 chunks (d = 128: 32 slices x 4), else 16 per round
   const bool small = p.T <= MTHREADS / 32 * 4;
+  const dim3 mgrid(p.H, p.B, p.d / MCOLS);
   if (p.d == 128) {
+    constexpr int NT = merge_threads<128>();
     if (small) {
-      if (p.bf16) merge_kernel<128, true, 4><<<grid, MTHREADS, 0, st>>>(p);
-      else merge_kernel<128, false, 4><<<grid, MTHREADS, 0, st>>>(p);
+      if (p.bf16) merge_kernel<128, true, 4><<<mgrid, NT, 0, st>>>(p);
+      else merge_kernel<128, false, 4><<<mgrid, NT, 0, st>>>(p);
     } else {
-      if (p.bf16) merge_kernel<128, true, 16><<<grid, MTHREADS, 0, st>>>(p);
-      else merge_kernel<128, false, 16><<<grid, MTHREADS, 0, st>>>(p);
+      if (p.bf16) merge_kernel<128, true, 16><<<mgrid, NT, 0, st>>>(p);
+      else merge_kernel<128, false, 16><<<mgrid, NT, 0, st>>>(p);
     }
   } else {
+    constexpr int NT = merge_threads<64>();
     if (small) {
-      if (p.bf16) merge_kernel<64, true, 4><<<grid, MTHREADS, 0, st>>>(p);
-      else merge_kernel<64, false, 4><<<grid, MTHREADS, 0, st>>>(p);
+      if (p.bf16) merge_kernel<64, true, 4><<<mgrid, NT, 0, st>>>(p);
+      else merge_kernel<64, false, 4><<<mgrid, NT, 0, st>>>(p);
     } else {
-      if (p.bf16) merge_kernel<64, true, 16><<<grid, MTHREADS, 0, st>>>(p);
-      else merge_kernel<64, false, 16><<<grid, MTHREADS, 0, st>>>(p);
+      if (p.bf16) merge_kernel<64, true, 16><<<mgrid, NT, 0, st>>>(p);
+      else merge_kernel<64, false, 16><<<mgrid, NT, 0, st>>>(p);
     }
   }
   return hipGetLastError();
