@@ -55,6 +55,9 @@ SMALL = [
     (1, 16, 2, 64, 20000, "bf16", "strat", 100, False, 4),  # 79 chunks: chunk CDF built in the sampling kernel
     (1, 8, 1, 128, 30000, "bf16", "iid", 64, False, 3),     # 118 chunks, G = 8
     (1, 14, 2, 128, 2100, "bf16", "strat", 64, True, 3),    # G = 7 with ternary queries
+    # T > 128: chunk CDF kernel, prefix rows read only for chunks that hold a point (G = 7 sys; iid)
+    (1, 7, 1, 64, 40000, "bf16", "sys", 48, False, 3),
+    (1, 8, 2, 64, 36000, "bf16", "iid", 40, False, 2),
     # B * Hkv * T = 3 * 8 * 100 = 2400 sampling blocks (> 2048): chunk CDF kernel with T <= 128, ragged tail
     (3, 16, 8, 64, 25563, "bf16", "strat", 64, False, 2),
     (3, 16, 8, 64, 25563, "bf16", "sys", 33, False, 2),
