@@ -323,7 +323,7 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
     }
     if constexpr (PER <= 0) {
       // with the chunk CDF known from the start, the prefix row is read only when one of the head's
-      // points falls in this chunk (most chunks hold none): the points are tested first, then found again
+      // points falls in this chunk (many chunks hold none): the points are tested first, then found again
       bool any = false;
       for (int c = lane; c < n; c += 64) {
         const double y = point_of(p, lo + c, h0 + g, b, u_sys) * Z;
