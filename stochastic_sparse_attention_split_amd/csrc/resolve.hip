@@ -231,7 +231,7 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
 
   // ---- the loads of the sampling phase (heads clamped to G - 1 and keys to the chunk's last key, so every
   //      address is valid): this wave's heads' chunk CDF inputs first, then, when the chunk CDF is built
-  //      here, its prefix rows at once (with a precomputed chunk CDF they are read below, once a point
+  //      here, its prefix rows at once (with a precomputed chunk CDF they are read per head once a point
   //      is known to fall in the chunk).
   //      Loads complete in issue order as far as the wait counter is concerned, so the chunk CDF can be
   //      built as soon as its few inputs have landed, while the prefix rows (the bulk of the bytes every
@@ -274,14 +274,6 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
   int jpf[HPW];  // a sampled key of each of this lane's heads (key 0 if none), for cache warming
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) jpf[hh] = 0;
-  // per head of this wave: the chunk's CDF edges and candidate points first; with a precomputed chunk CDF
-  // the prefix rows of the heads that have a point here are then requested together, so their latencies
-  // overlap, and the points are searched in a second pass
-  double pc0[HPW], pc1[HPW], pZ[HPW], pf[HPW], pus[HPW];
-  int plast[HPW], plo[HPW], pn[HPW];
-  bool hpt[HPW];
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) hpt[hh] = false;
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     const int g = wave + NWAVE * hh;
@@ -303,6 +295,15 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
       f = eF[hh];
       lastc = eL[hh];
     }
+    // this head's prefix row, written and then searched by this wave only
+    if constexpr (PER > 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Pt[g][4 * lane + i] = pv[hh][i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
     if (p.prob) {  // debug: probabilities of this chunk's keys from the score pass's exponentials
       double* pr = p.prob + (bh0 + g) * p.nk + n0;
       for (int k = lane; k < len; k += 64) pr[k] = pr[k] * f / Z;
@@ -320,43 +321,25 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
         n = ihi >= ilo ? ihi - ilo + 1 : 0;
       }
     }
-    pc0[hh] = c0;
-    pc1[hh] = c1;
-    pZ[hh] = Z;
-    pf[hh] = f;
-    pus[hh] = u_sys;
-    plast[hh] = lastc;
-    plo[hh] = lo;
-    pn[hh] = n;
-    hpt[hh] = true;
     if constexpr (PER <= 0) {
-      // the prefix row is read only when one of the head's points falls in this chunk (many chunks hold
-      // none): the points are tested here and found again in the second pass
+      // with the chunk CDF known from the start, the prefix row is read only when one of the head's
+      // points falls in this chunk (many chunks hold none): the points are tested first, then found again
       bool any = false;
       for (int c = lane; c < n; c += 64) {
         const double y = point_of(p, lo + c, h0 + g, b, u_sys) * Z;
         any = any || (y < Z ? (c0 <= y && y < c1) : (t == lastc));
       }
-      hpt[hh] = __ballot(any) != 0ull;  // wave-uniform
-      if (hpt[hh]) {
-        const int64_t bh = bh0 + g;
+      if (__ballot(any) == 0ull) continue;  // wave-uniform
+      const int64_t bh = bh0 + g;
+      double v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pv[hh][i] = p.stash[bh * p.stash_stride + n0 + min(4 * lane + i, len - 1)];
-      }
+      for (int i = 0; i < 4; ++i) v[i] = p.stash[bh * p.stash_stride + n0 + min(4 * lane + i, len - 1)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Pt[g][4 * lane + i] = v[i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-  }
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    if (!hpt[hh]) continue;  // wave-uniform
-    const int g = wave + NWAVE * hh;
-    const double c0 = pc0[hh], c1 = pc1[hh], Z = pZ[hh], f = pf[hh], u_sys = pus[hh];
-    const int lastc = plast[hh], lo = plo[hh], n = pn[hh];
-    // this head's prefix row, written and then searched by this wave only
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Pt[g][4 * lane + i] = pv[hh][i];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     for (int c = lane; c < n; c += 64) {
       const int m = lo + c;
       const double y = point_of(p, m, h0 + g, b, u_sys) * Z;
