@@ -402,11 +402,10 @@ __device__ inline void wait_vm() {
   else static_assert(N == 0, "unsupported count");
 }
 
-constexpr int SQUART = 4;                // key quarters of a chunk (64 keys each)
-constexpr int SMFMA = 2 * SQUART;        // matrix-core waves: (key quarter, half of the head dimension)
-constexpr int SSOFT = 4;                 // exponential waves: one head each
+constexpr int SQUART = 4;                // key quarters of a chunk (64 keys each): one matrix wave each
+constexpr int SSOFT = 4;                 // exponential waves: one head each (two for G = 5..8)
 constexpr int SCOPY = 4;                 // copy waves: two per K tile
-constexpr int STHREADS = 64 * (SMFMA + SSOFT + SCOPY);  // 16 waves: four per SIMD
+constexpr int STHREADS = 64 * (SQUART + SSOFT + SCOPY);  // 12 waves: three per SIMD
 constexpr int SPIN_LIMIT = 1 << 22;      // bounded waits: a stuck handshake ends the kernel, flagged
 
 template <int D>
@@ -446,37 +445,29 @@ __device__ inline bool wait_ge(int* ctr, int target) {
   return true;
 }
 
-// Streaming score pass for bf16 caches and G <= 8, one block per CU, three roles that meet only through
-// LDS counters (no block-wide barrier after the start), so the K stream, the matrix cores and the
-// exponentials overlap. The 16-wave layout below serves the fused S²ANTA-flash pass; every other call
-// runs the 12-wave full-row form (FD, further down) with the same exponential and copy roles:
-//   * waves 0..7 (two per SIMD): fp64 MFMA over key quarter w & 3 (64 keys: four 16-key groups) and
-//     half w >> 2 of the head dimension (element parity gives eight independent accumulation chains per
-//     wave); each writes its partial dot products into the partial row of its half. Two waves per SIMD
-//     keep the fp64 matrix pipe busy where one wave alone leaves it idle between dependent MFMAs, and
-//     neither waits for the other;
-//   * waves 8..11: score = lower + upper partial (a fixed order), then chunk max, exponentials,
-//     in-chunk prefix and the stores of head w - 8;
-//   * waves 12..15: global -> LDS copies (global_load_lds) of the K tiles, waves 12-13 tile 0 with the
-//     block's even chunks, 14-15 tile 1 with the odd ones (wave 14 first copies the queries). The first
+// Streaming score pass for bf16 caches and G <= 8, one block of 12 waves per CU (one wave of each role
+// per SIMD), three roles that meet only through LDS counters (no block-wide barrier after the start), so
+// the K stream, the matrix cores and the exponentials overlap:
+//   * waves 0..3: fp64 MFMA over key quarter w (64 keys: four 16-key groups) and the whole head dimension
+//     (element parity gives eight independent accumulation chains per head group), writing complete
+//     scores. Two half-row waves per SIMD keep the matrix pipe busier on their own, but beside the K
+//     stream writing into LDS one whole-row wave is no slower, and no partial rows need adding. For
+//     G = 5..8 (HG = 2) the wave scores both head groups: each K element is converted once for the
+//     MFMAs of the eight heads, and the query operands are read from LDS per 4-piece step to stay within
+//     the register budget of three waves per SIMD;
+//   * waves 4..7: chunk max, exponentials, in-chunk prefix and the stores of head w - 4 (and w for
+//     G = 5..8);
+//   * waves 8..11: global -> LDS copies (global_load_lds) of the K tiles, waves 8-9 tile 0 with the
+//     block's even chunks, 10-11 tile 1 with the odd ones (wave 10 first copies the queries). The first
 //     chunk of tile 1 is requested only once tile 0 has landed, so across the device the first tiles
 //     arrive before any second one and the matrix cores start half a pass earlier.
 // Counters (chunk k lives in tile k & 1; its fill index there is k >> 1):
 //   ld[j] +1 per copy wave when its half of tile j's current chunk has landed;
 //   use[j] +1 per MFMA wave when its reads of tile j are done;  pr +1 per MFMA wave per chunk whose
-//   partials are written;  pc +1 per exponential wave per chunk whose partials it has read;  qr queries
+//   scores are written;  pc +1 per exponential wave per chunk whose scores it has read;  qr queries
 //   landed;  pb prologue barrier;  fin waves finished (the last one publishes the block's handshake
 //   status).
-// HG = head groups of four (G <= 4 * HG). Without FD (the fused S²ANTA-flash pass, G <= 4) the MFMA wave
-// pair of a key quarter splits the head dimension and the exponential wave adds the two partial rows.
-// With HG = 2 (G = 5..8) each exponential wave handles heads g and g + 4.
-// FD (full rows, without S²ANTA-flash): four matrix waves, one per SIMD, each over its key quarter
-// and the whole head dimension, writing complete scores; the exponential waves are waves 4..7 and the copy
-// waves 8..11 (a 768-thread block). With the K stream writing into LDS, one matrix wave per SIMD over
-// whole rows is no slower than two over half rows, and the partial rows and their addition disappear.
-// With HG = 2 the wave scores both head groups: each K element is converted once for the MFMAs of the
-// eight heads (the query operands are read from LDS per 4-piece step to stay within the register budget
-// of three waves per SIMD), and its sums run in the same order as the HG = 2 pair's.
+// HG = head groups of four (G <= 4 * HG).
 // FL: S²ANTA-flash kernel 1 ("Stochastic Sparse Attention for Memory-Bound Inference", Section 3.3 and
 // Appendix P, Algorithm 7) fused in: right after a chunk's exponentials, the exponential wave of head g
 // takes the tile's systematic counts with the uniform budget S_tile (c_n = floor(a0 + inv P_n) -
@@ -484,23 +475,21 @@ __device__ inline bool wait_ge(int* ctr, int target) {
 // counter (t, h, b, 4)), writes the index slots and the tile's sampled-key bits, and issues the loads of
 // its sampled V rows; one chunk later (the loads have landed meanwhile) it adds count x row into the fp32
 // tile partial and stores it. Only the merge kernel follows: two launches per decode step.
-template <int D, int HG, bool FL, bool FD = false>
-__global__ __launch_bounds__(64 * ((FD ? SQUART : SMFMA) + SSOFT + SCOPY), 1) void score_stream_kernel(Problem p) {
+template <int D, int HG, bool FL>
+__global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   static_assert(!FL || HG == 1, "the fused S²ANTA-flash form covers G <= 4");
-  static_assert(!FD || !FL, "the full-row form does not take the fused S²ANTA-flash pass");
-  static_assert(FD || HG == 1, "G = 5..8 runs in the full-row form");
-  constexpr int NMF = FD ? SQUART : SMFMA;  // matrix-core waves
+  constexpr int NMF = SQUART;  // matrix-core waves
   constexpr int NTH = 64 * (NMF + SSOFT + SCOPY);
   using Sg = SGeo<D>;
   constexpr int EPL = 8, PPH = Sg::PPH, CPW = Sg::CPW;
   constexpr int KPW = CHUNK / SQUART;  // keys per MFMA wave
   constexpr int NGR = KPW / 16;       // 16-key groups per MFMA wave
   constexpr int HM = 4 * HG;          // heads held
-  constexpr int NPW = HG == 1 && !FD ? PPH : 2 * PPH;  // 4-piece steps of a row per MFMA wave
+  constexpr int NPW = 2 * PPH;       // 4-piece steps of a row per MFMA wave
   static_assert(D * 2 * HM <= 1024 * HG, "the queries of a group fit HG 1 KiB copies");
 
   __shared__ __align__(16) unsigned char kt[2][Sg::TILE];
-  __shared__ __align__(16) double part[2][4][CHUNK];  // [half of d | head group][head][key]
+  __shared__ __align__(16) double part[HG][4][CHUNK];  // scores: [head group][head][key]
   __shared__ __align__(16) double qe[HM][D + 2];
   __shared__ double hnorm[HM];
   __shared__ __align__(16) unsigned char qs[1024 * HG];
@@ -623,7 +612,7 @@ __global__ __launch_bounds__(64 * ((FD ? SQUART : SMFMA) + SSOFT + SCOPY), 1) vo
   }
 
   if (wave >= NMF) {
-    // ---- exponential waves: heads w - 8 (+ 4) of every chunk, lane owns keys 4*lane .. 4*lane + 3. Issue
+    // ---- exponential waves: heads w - 4 (+ 4) of every chunk, lane owns keys 4*lane .. 4*lane + 3. Issue
     // priority above the MFMA waves sharing their SIMD, whose instruction stream would otherwise starve them.
     __builtin_amdgcn_s_setprio(2);
     const int g0 = wave - NMF;
@@ -672,21 +661,12 @@ __global__ __launch_bounds__(64 * ((FD ? SQUART : SMFMA) + SSOFT + SCOPY), 1) vo
       double raw[HG][4];
 #pragma unroll
       for (int hx = 0; hx < HG; ++hx) {
-        const double2* lo = (const double2*)&part[HG == 1 ? 0 : hx][g0][4 * lane];
+        const double2* lo = (const double2*)&part[hx][g0][4 * lane];
         const double2 l0 = lo[0], l1 = lo[1];
-        if constexpr (HG == 1 && !FD) {  // lower + upper half of the head dimension
-          const double2* hi = (const double2*)&part[1][g0][4 * lane];
-          const double2 h0v = hi[0], h1v = hi[1];
-          raw[hx][0] = l0.x + h0v.x;
-          raw[hx][1] = l0.y + h0v.y;
-          raw[hx][2] = l1.x + h1v.x;
-          raw[hx][3] = l1.y + h1v.y;
-        } else {
-          raw[hx][0] = l0.x;
-          raw[hx][1] = l0.y;
-          raw[hx][2] = l1.x;
-          raw[hx][3] = l1.y;
-        }
+        raw[hx][0] = l0.x;
+        raw[hx][1] = l0.y;
+        raw[hx][2] = l1.x;
+        raw[hx][3] = l1.y;
       }
       signal(pc, lane);  // the partial rows have been read
       const int t = t0 + k * step;
@@ -837,7 +817,7 @@ __global__ __launch_bounds__(64 * ((FD ? SQUART : SMFMA) + SSOFT + SCOPY), 1) vo
 
   // ---- MFMA waves: 16-key groups x element parity = independent accumulation chains
   const int slot = lane >> 4;
-  if constexpr (FD && HG == 2) {
+  if constexpr (HG == 2) {
     const int quart = wave;
     for (int k = 0; k < n && ok; ++k) {
       ok = wait_ge(&ld[k & 1], 2 * ((k >> 1) + 1));  // chunk k's tile has landed
@@ -884,15 +864,14 @@ __global__ __launch_bounds__(64 * ((FD ? SQUART : SMFMA) + SSOFT + SCOPY), 1) vo
     finish();
     return;
   }
-  // key quarter; half of the head dimension (HG = 1) or head group (HG = 2)
-  const int quart = FD ? wave : wave & (SQUART - 1), dh = FD ? 0 : wave / SQUART;
-  const int pbase = HG == 1 && !FD ? dh * PPH : 0;  // first 4-piece step of this wave's part of a row
-  const int qrow = HG == 1 ? (lane & 3) : 4 * dh + (lane & 3);
+  // key quarter over the whole head dimension (HG = 1)
+  const int quart = wave;
+  const int qrow = lane & 3;
   double qb[NPW][EPL];
 #pragma unroll
   for (int pp = 0; pp < NPW; ++pp)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qb[pp][e] = qe[qrow][EPL * (4 * (pbase + pp) + slot) + e];
+    for (int e = 0; e < EPL; ++e) qb[pp][e] = qe[qrow][EPL * (4 * pp + slot) + e];
   for (int k = 0; k < n && ok; ++k) {
     ok = wait_ge(&ld[k & 1], 2 * ((k >> 1) + 1));  // chunk k's tile has landed
     if (!ok) break;
@@ -905,7 +884,7 @@ __global__ __launch_bounds__(64 * ((FD ? SQUART : SMFMA) + SSOFT + SCOPY), 1) vo
       uint4 a4[NGR];
 #pragma unroll
       for (int gi = 0; gi < NGR; ++gi)
-        a4[gi] = *(const uint4*)(ks + tile_off<D>(quart * KPW + gi * 16 + (lane & 15), 4 * (pbase + pp) + slot));
+        a4[gi] = *(const uint4*)(ks + tile_off<D>(quart * KPW + gi * 16 + (lane & 15), 4 * pp + slot));
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
 #pragma unroll
@@ -919,7 +898,7 @@ __global__ __launch_bounds__(64 * ((FD ? SQUART : SMFMA) + SSOFT + SCOPY), 1) vo
 #pragma unroll
     for (int gi = 0; gi < NGR; ++gi) {
       const int key = quart * KPW + gi * 16 + 4 * ((lane >> 2) & 3) + (lane >> 4);
-      part[dh][lane & 3][key] = acc[gi][0] + acc[gi][1];
+      part[0][lane & 3][key] = acc[gi][0] + acc[gi][1];
     }
     signal(pr, lane);
   }
@@ -945,11 +924,9 @@ hipError_t launch_d(const Problem& p, hipStream_t st, const LaunchEvents& ev) {
     const dim3 grid(p.score_blocks_per_group, p.Hkv, p.B);
     if (p.G <= 4) {
       if (p.fused) return launch_timed(score_stream_kernel<D, 1, true>, grid, dim3(STHREADS), st, ev, p);
-      return launch_timed(score_stream_kernel<D, 1, false, true>, grid, dim3(64 * (SQUART + SSOFT + SCOPY)), st, ev,
-                          p);
+      return launch_timed(score_stream_kernel<D, 1, false>, grid, dim3(STHREADS), st, ev, p);
     }
-    return launch_timed(score_stream_kernel<D, 2, false, true>, grid, dim3(64 * (SQUART + SSOFT + SCOPY)), st, ev,
-                        p);
+    return launch_timed(score_stream_kernel<D, 2, false>, grid, dim3(STHREADS), st, ev, p);
   }
   return p.G <= 4 ? launch_q<D, BF16, 1>(p, st, ev) : launch_q<D, BF16, 2>(p, st, ev);
 }
