@@ -155,6 +155,22 @@ int santa_decode(const void* q, const void* K, const void* V, int64_t nk, int he
  */
 int santa_decode_ex(const santa_args* a);
 
+/*
+ * santa_decode_noalloc — santa_decode_ex for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. It takes the same arguments but
+ * ignores `workspace` / `workspace_bytes`: its workspace is a SANTA_NOALLOC_MAX_BYTES device array of
+ * the library (one per device, created when the library's code object is loaded on that device and held
+ * until the process ends; its address is looked up once per device on the first call there). The call
+ * allocates nothing. The caller still passes q, K, V, out and the optional device idx_out / prob_out.
+ * Errors: SANTA_ERR_WORKSPACE when santa_workspace_bytes() for these sizes exceeds
+ * SANTA_NOALLOC_MAX_BYTES; SANTA_ERR_INVALID_ARG when stats_out or stage_ms is set (they synchronise and
+ * create events); otherwise as santa_decode_ex. Every call on one device shares that device's array, so
+ * calls that overlap on one device (other streams, other threads) race; calls in one stream do not.
+ * No initial contents are required: each call writes every part of the array it later reads.
+ */
+#define SANTA_NOALLOC_MAX_BYTES (64u << 20)
+int santa_decode_noalloc(const santa_args* a);
+
 /* Workspace bytes santa_decode_ex needs for these sizes (0 if the sizes are invalid or d is unsupported). */
 size_t santa_workspace_bytes(int batch, int64_t nk, int heads, int kv_heads, int d, int S, int mode);
 

@@ -5,6 +5,7 @@ device memory and the current stream. The entry points mirror include/santa.h:
 
     decode(q, K, V, S, mode, seed, ...)      -> santa_decode_ex
     decode_simple(q, K, V, S, mode, seed)    -> santa_decode (library-owned workspace, batch 1, bf16)
+    decode_noalloc(q, K, V, S, mode, seed)   -> santa_decode_noalloc (the library's static device scratch)
     dense_decode(q, K, V, ...)               -> santa_dense_decode (dense baseline)
     workspace_bytes(...), dense_workspace_bytes(...), philox4x32_10(ctr, key), version(), last_error()
 
@@ -37,7 +38,7 @@ EXPORTED = [
     "santa_decode", "santa_decode_ex", "santa_workspace_bytes", "santa_dense_decode",
     "santa_dense_workspace_bytes", "santa_philox4x32_10", "santa_exp_f64", "santa_status_string", "santa_last_error",
     "santa_version", "santa_release", "santa_samples_per_head", "santa_stream_read",
-    "santa_stream_read_scratch_bytes",
+    "santa_stream_read_scratch_bytes", "santa_decode_noalloc",
 ]
 
 
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_void_p]
         L.santa_decode_ex.restype = ctypes.c_int
         L.santa_decode_ex.argtypes = [ctypes.POINTER(SantaArgs)]
+        L.santa_decode_noalloc.restype = ctypes.c_int
+        L.santa_decode_noalloc.argtypes = [ctypes.POINTER(SantaArgs)]
         L.santa_dense_decode.restype = ctypes.c_int
         L.santa_dense_decode.argtypes = [ctypes.POINTER(SantaArgs)]
         L.santa_samples_per_head.restype = ctypes.c_int64
@@ -202,6 +205,18 @@ def _fill_common(a: SantaArgs, q, K, V, out, nk, stream, k_feature_major: bool =
     a.stream = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
+def _set_debug_outputs(a: SantaArgs, idx_out, prob_out):
+    if idx_out is not None:
+        L = int(lib().santa_samples_per_head(a.nk, a.S, a.mode))
+        if idx_out.dtype != torch.int32 or idx_out.numel() < a.batch * a.heads * L:
+            raise ValueError(f"idx_out must be int32 with batch*heads*{L} elements")
+        a.idx_out = idx_out.data_ptr()
+    if prob_out is not None:
+        if prob_out.dtype != torch.float64 or prob_out.numel() < a.batch * a.heads * a.nk:
+            raise ValueError("prob_out must be float64 with batch*heads*nk elements")
+        a.prob_out = prob_out.data_ptr()
+
+
 def decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="strat", seed: int = 0, *,
            ternary: bool = False, nk: int | None = None, out: torch.Tensor | None = None,
            workspace: torch.Tensor | None = None, idx_out: torch.Tensor | None = None,
@@ -229,15 +244,7 @@ def decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="stra
         workspace = new_workspace(need, q.device)
     a.workspace = workspace.data_ptr()
     a.workspace_bytes = workspace.numel() * workspace.element_size()
-    if idx_out is not None:
-        L = int(lib().santa_samples_per_head(a.nk, a.S, a.mode))
-        if idx_out.dtype != torch.int32 or idx_out.numel() < a.batch * a.heads * L:
-            raise ValueError(f"idx_out must be int32 with batch*heads*{L} elements")
-        a.idx_out = idx_out.data_ptr()
-    if prob_out is not None:
-        if prob_out.dtype != torch.float64 or prob_out.numel() < a.batch * a.heads * a.nk:
-            raise ValueError("prob_out must be float64 with batch*heads*nk elements")
-        a.prob_out = prob_out.data_ptr()
+    _set_debug_outputs(a, idx_out, prob_out)
     st = SantaStats()
     ms = (ctypes.c_float * 4)()
     if stats:
@@ -252,6 +259,25 @@ def decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="stra
         if stage_ms:
             info["stage_ms"] = list(ms)
         return out, info
+    return out
+
+
+def decode_noalloc(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="strat", seed: int = 0, *,
+                   out: torch.Tensor, ternary: bool = False, nk: int | None = None,
+                   idx_out: torch.Tensor | None = None, prob_out: torch.Tensor | None = None, stream=None,
+                   group_bernoulli: int = 0, k_feature_major: bool = False):
+    """One decode step through santa_decode_noalloc: the workspace is the library's own device array, so
+    the call allocates nothing (``out`` must be given; no stats or stage timing)."""
+    a = SantaArgs()
+    _fill_common(a, q, K, V, out, nk, stream, k_feature_major)
+    a.S = int(S)
+    a.mode = _mode_code(mode, ternary) | (K_FEATURE_MAJOR if k_feature_major else 0)
+    if group_bernoulli:
+        a.mode |= GROUP_BERNOULLI_Q
+        a.bern_samples = int(group_bernoulli)
+    a.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    _set_debug_outputs(a, idx_out, prob_out)
+    _check(lib().santa_decode_noalloc(ctypes.byref(a)))
     return out
 
 

@@ -383,6 +383,56 @@ int santa_decode(const void* q, const void* K, const void* V, int64_t nk, int he
   return santa_decode_ex(&a);
 }
 
+// ---- entry point without allocation: the workspace is the library's own device array
+
+// One copy per device, zero-initialised when the code object is loaded and held until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: only the address
+// hipGetSymbolAddress returns for the current device is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[SANTA_NOALLOC_MAX_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // per device: the device address of `scratch`
+
+// device address of `scratch` on the current device, looked up once per device with that device current
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess)
+      return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(SANTA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SANTA_OK;
+}
+}  // namespace
+
+int santa_decode_noalloc(const santa_args* a) {
+  g_err.clear();
+  if (!a) return fail(SANTA_ERR_INVALID_ARG, "args is NULL");
+  if (a->stats_out || a->stage_ms)
+    return fail(SANTA_ERR_INVALID_ARG, "santa_decode_noalloc takes no host debug outputs (stats_out, stage_ms)");
+  int64_t seq = 0, bstride = 0, kt_row = 0, kt_batch = 0;
+  int st = validate_sampled(a, &seq, &bstride, &kt_row, &kt_batch);
+  if (st) return st;
+  const size_t need = layout(a->batch, a->nk, a->heads, a->kv_heads, a->d, a->S, a->mode).total;
+  if (need > (size_t)SANTA_NOALLOC_MAX_BYTES)
+    return fail(SANTA_ERR_WORKSPACE, "these sizes need %zu bytes of scratch; santa_decode_noalloc holds %zu",
+                need, (size_t)SANTA_NOALLOC_MAX_BYTES);
+  void* ptr = nullptr;
+  if ((st = scratch_address(&ptr))) return st;
+  santa_args b = *a;
+  b.workspace = ptr;
+  b.workspace_bytes = SANTA_NOALLOC_MAX_BYTES;
+  return santa_decode_ex(&b);
+}
+
 void santa_release(void) {
   std::lock_guard<std::mutex> lock(g_ws_mu);
   int cur = 0;

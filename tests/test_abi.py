@@ -201,3 +201,20 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(santa, "LIB_PATH", "/nonexistent/libsanta.so")
     with pytest.raises(RuntimeError):
         santa.lib()
+
+
+def test_noalloc_validation_before_any_hip_call(L):
+    """santa_decode_noalloc checks its arguments and the size of its static scratch before any HIP call."""
+    assert L.santa_decode_noalloc(None) == santa.ERR_INVALID_ARG
+    a = _args(heads=6, kv_heads=4)
+    assert L.santa_decode_noalloc(ctypes.byref(a)) == santa.ERR_INVALID_ARG
+    st = santa.SantaStats()
+    a = _args(stats_out=ctypes.pointer(st))
+    assert L.santa_decode_noalloc(ctypes.byref(a)) == santa.ERR_INVALID_ARG
+    assert "debug" in santa.last_error()
+    a = _args(stage_ms=(ctypes.c_float * 4)())
+    assert L.santa_decode_noalloc(ctypes.byref(a)) == santa.ERR_INVALID_ARG
+    # 8 sequences of 2^20 keys need far more than the scratch holds; workspace fields are ignored
+    a = _args(batch=8, nk=1 << 20, heads=32, kv_heads=8, workspace=0, workspace_bytes=0)
+    assert L.santa_decode_noalloc(ctypes.byref(a)) == santa.ERR_WORKSPACE
+    assert "santa_decode_noalloc holds" in santa.last_error()
