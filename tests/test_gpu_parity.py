@@ -305,13 +305,14 @@ def test_workload_2_full_size():
     assert rep["mismatches"] == 0
 
 
-def test_workload_3_full_size_sweep():
+@pytest.mark.parametrize("S", [64, 128, 256, 512, 1024])
+def test_workload_3_full_size_sweep(S):
+    """Batched decode at full size (B8, nk 32768 per sequence, systematic), every S of the sweep."""
     w = workloads.make(3)
-    log(f"workload 3 {w.name}: B{w.B} nk{w.nk} sys S in {w.S_sweep}")
-    for i, S in enumerate((64, 256, 1024)):
-        rep, *_ = compare(w.q, w.K, w.V, S, w.mode, w.seed, dtype=w.dtype, want_prob=(i == 0),
-                          label=f"{w.name} S={S}")
-        log(f"  S={S}: {rep}")
+    log(f"workload 3 {w.name}: B{w.B} nk{w.nk} sys S={S}")
+    rep, *_ = compare(w.q, w.K, w.V, S, w.mode, w.seed, dtype=w.dtype, want_prob=(S == 64),
+                      label=f"{w.name} S={S}")
+    log(f"  S={S}: {rep}")
 
 
 def test_workload_3_reduced_nk_all_S():

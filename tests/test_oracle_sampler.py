@@ -250,3 +250,31 @@ def test_strat_and_sys_indices_are_nondecreasing():
         for seed in range(10):
             J, _ = oracle.inverse_cdf(F, p, oracle.sample_points(mode, 97, seed, 1, 2))
             assert np.all(np.diff(J) >= 0)
+
+
+def test_iid_frequencies_match_torch_multinomial():
+    """The i.i.d. sampler draws indices with the semantics of torch.multinomial(p, S, replacement=True)
+    (the code on the alphasignal summary page): a two-sample chi-square test of the oracle's index counts
+    against torch's over 40 960 draws from a peaked 12-key softmax, plus each against p itself."""
+    import torch
+    from scipy import stats
+
+    rng = np.random.default_rng(11)
+    s = rng.standard_normal(12) * 2.0
+    p, _, _ = oracle.softmax(s)
+    F = oracle.cdf(p)
+    S, reps = 4096, 10
+    counts = np.zeros(12, dtype=np.int64)
+    for seed in range(reps):
+        T = oracle.sample_points(oracle.IID, S, seed, 0, 0)
+        J, _ = oracle.inverse_cdf(F, p, T)
+        counts += np.bincount(J, minlength=12)
+    gen = torch.Generator().manual_seed(1234)
+    tm = torch.multinomial(torch.tensor(p), S * reps, replacement=True, generator=gen).numpy()
+    tcounts = np.bincount(tm, minlength=12)
+    n = S * reps
+    keep = p * n >= 5  # chi-square cells with enough expected mass
+    _, pv_two, _, _ = stats.chi2_contingency(np.stack([counts[keep], tcounts[keep]]))
+    assert pv_two > 1e-3, pv_two
+    for c in (counts, tcounts):
+        assert stats.chisquare(c[keep], p[keep] / p[keep].sum() * c[keep].sum()).pvalue > 1e-3

@@ -87,3 +87,24 @@ def test_figure6_error_level_B4():
         errs.append(np.linalg.norm(phat - p) / np.linalg.norm(p))
     level = float(np.mean(errs))
     assert abs(level - g["standard_rel_l2"]) < 0.08
+
+
+def test_figure6_stratified_level_B4():
+    """Figure 6 and Appendix C.1: stratified Bernoulli sampling at B = 4 gives about 30% mean relative L2
+    error of the score estimate (dk=128, nk=1024). The stratified estimator is the mean-group-query one
+    with a group of a single query (m = |q|, norm = max|q|, per-feature stratified counts)."""
+    g = json.load(open(os.path.join(HERE, "golden", "fig6_bernoulli.json")))
+    rng = np.random.default_rng(7)
+    dk, nk, inst, B = g["dk"], g["nk"], g["instances"], g["B"]
+    errs = []
+    for i in range(inst):
+        q = rng.standard_normal(dk)
+        K = rng.standard_normal((nk, dk)) / np.sqrt(dk)
+        exact = (K @ q) * oracle.scale(dk)
+        s, c, norm = oracle.group_bernoulli.group_scores(q[None, :], K, B, 2000 + i, 0, 0)
+        assert norm == np.max(np.abs(q)) and c.min() >= 0 and c.max() <= B
+        errs.append(np.linalg.norm(s[0] - exact) / np.linalg.norm(exact))
+    level = float(np.mean(errs))
+    assert abs(level - g["stratified_rel_l2"]) < 0.08, level
+    # and stratification halves the i.i.d. level the same figure prints
+    assert level < 0.75 * g["standard_rel_l2"]
