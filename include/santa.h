@@ -50,6 +50,10 @@ extern "C" {
 #define SANTA_ERR_UNSUPPORTED 2     /* d not in {64, 128}, dtype, G > 8, nk > 2^20, S > 65535 */
 #define SANTA_ERR_WORKSPACE 3       /* workspace_bytes smaller than santa_workspace_bytes() */
 #define SANTA_ERR_HIP 4             /* a HIP runtime call or launch failed (see santa_last_error) */
+#define SANTA_ERR_TIMEOUT 5         /* a bounded in-kernel wait gave up (blocks of one launch that were not all
+                                       resident, or a handshake that never completed); the outputs of the
+                                       affected query heads are NaN. Reported by santa_status() and by calls
+                                       with stats_out. */
 
 /* sampling modes (low byte) and flags */
 #define SANTA_IID 0                 /* SANTA: T_m ~ U[0,1) i.i.d. (Section 2, Eq. 4) */
@@ -81,6 +85,9 @@ extern "C" {
                                        element (b, kv, i, n) at K[b * kt_batch_stride + (kv * d + i) *
                                        kt_row_stride + n]; V keeps the sequence-major layout. The score pass
                                        then reads only the feature rows with a non-zero query weight. */
+#define SANTA_MULTI_LAUNCH 0x800    /* use the multi-launch path (score, sampling and merge kernels) even where
+                                       the one-launch decode applies; same results up to the order of the fp32
+                                       partial sums (a measurement and diagnosis option) */
 
 /* element types of q, K, V and out */
 #define SANTA_BF16 0
@@ -93,6 +100,9 @@ typedef struct santa_stats {
   int64_t bytes_v;       /* V bytes gathered: (sum over (b, kv) of distinct sampled rows) * d * elt */
   int64_t bytes_qo;      /* q read + out written: 2 * batch * heads * d * elt */
   int64_t unique_rows;   /* sum over (b, kv) of the distinct sampled rows */
+  int64_t* group_unique_rows;  /* optional host array [batch * kv_heads] (NULL to skip): the distinct sampled
+                                  rows of each (sequence, KV head), the rows its gather reads (Appendix O,
+                                  Algorithm 5, the emitted rows of the group) */
 } santa_stats;
 
 typedef struct santa_args {
@@ -125,15 +135,28 @@ typedef struct santa_args {
   double* prob_out;          /* device [batch, heads, nk]: softmax probabilities */
   santa_stats* stats_out;    /* host; the call synchronises the stream to fill it */
   float* stage_ms;           /* host float[4], milliseconds; synchronises the stream. [0]: execution time of
-                                the score kernel (events HIP records at the kernel's own start and end);
-                                [1]: from the end of the score kernel to an event after the chunk CDF and
-                                resolve launches; [2]: from there to an event after the merge launch;
-                                [3]: from the score kernel's start to that last event */
+                                the score kernel (events HIP records at the kernel's own start and end; the
+                                whole decode for the one-launch form); [1]: from the end of the score
+                                kernel to an event after the chunk CDF and resolve launches; [2]: from there
+                                to an event after the merge launch; [3]: from the score kernel's start to
+                                that last event */
   /* SANTA_K_FEATURE_MAJOR only (elements); rows must hold at least nk rounded up to 8 and start 16-byte
      aligned */
   int64_t kt_row_stride;     /* between feature rows; 0 means nk rounded up to 8 */
   int64_t kt_batch_stride;   /* between sequences; 0 means kv_heads * d * kt_row_stride */
+  int32_t debug_spin_limit;  /* polls before a bounded in-kernel wait gives up; 0 = the library default (a
+                                wait of seconds). Tests set small values to force the timeout path, whose
+                                outputs are NaN and whose status is SANTA_ERR_TIMEOUT. */
 } santa_args;
+
+/*
+ * santa_status — the outcome of the last call that used this workspace with these sizes: synchronises
+ * a->stream, then returns SANTA_OK, or SANTA_ERR_TIMEOUT if a bounded in-kernel wait of any (sequence, KV
+ * head) group gave up in that call (those heads' outputs are NaN). a->workspace NULL means the scratch of
+ * santa_decode_noalloc on the current device. Every decode call writes these status words, so the
+ * default path needs no stats_out to detect the failure.
+ */
+int santa_status(const santa_args* a);
 
 /*
  * santa_decode — one SANTA / S²ANTA decode step in its simplest form: batch 1, bf16 q/K/V/out,
@@ -146,12 +169,21 @@ int santa_decode(const void* q, const void* K, const void* V, int64_t nk, int he
 
 /*
  * santa_decode_ex — the full form. Caller-owned workspace (`workspace`, `workspace_bytes`); never
- * allocates device memory. Launches three or four kernels on `stream`: the split-K score pass; for more
- * than 128 chunks of 256 keys, the chunk CDF per KV group (SANTA_PROP: the tile budgets per query head;
- * SANTA_FLASH needs neither), which the next kernel otherwise builds itself; the sampling and gather-add per (chunk, KV group) (each
+ * allocates device memory. Calls sharing one workspace must not overlap.
+ * One launch where it applies (bf16, sequence-major K, SANTA_IID / STRAT / SYS, at most one block per CU
+ * for the whole grid, up to 512 chunks of 256 keys per sequence, and the block's chunks fit the sampling
+ * phase's LDS): the split-K score pass, then, after in-kernel barriers between the blocks of each (KV head,
+ * sequence) group (Section 3.1's global barrier, per group), the chunk CDF, the points that fall in each
+ * block's chunks, the gather of each distinct sampled row once per group into fp32 sums per head, and the
+ * sum of the blocks' partials per head times 1/S. These barriers need every block of the launch resident
+ * at once; if other work keeps blocks from running, the bounded waits give up and the call reports
+ * SANTA_ERR_TIMEOUT (santa_status) with NaN outputs.
+ * Otherwise three or four kernels on `stream`: the split-K score pass; for more than 128 chunks of 256
+ * keys, the chunk CDF per KV group (SANTA_PROP: the tile budgets per query head; SANTA_FLASH needs neither),
+ * which the next kernel otherwise builds itself; the sampling and gather-add per (chunk, KV group) (each
  * distinct sampled row read once and added with its per-head counts into an fp32 chunk partial); and the
  * merge that adds the chunk partials of each head and scales by 1/S (SANTA_FLASH: weights each partial by
- * W_t / (Z S_tile)). Calls sharing one workspace must not overlap.
+ * W_t / (Z S_tile)).
  */
 int santa_decode_ex(const santa_args* a);
 

@@ -26,11 +26,12 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsanta.so")
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_TIMEOUT = 0, 1, 2, 3, 4, 5
 IID, STRAT, SYS, PROP, FLASH = 0, 1, 2, 3, 4
 TERNARY_Q = 0x100
 GROUP_BERNOULLI_Q = 0x200
 K_FEATURE_MAJOR = 0x400
+MULTI_LAUNCH = 0x800
 BF16, F32 = 0, 1
 MODES = {"iid": IID, "strat": STRAT, "sys": SYS, "prop": PROP, "flash": FLASH}
 
@@ -38,13 +39,14 @@ EXPORTED = [
     "santa_decode", "santa_decode_ex", "santa_workspace_bytes", "santa_dense_decode",
     "santa_dense_workspace_bytes", "santa_philox4x32_10", "santa_exp_f64", "santa_status_string", "santa_last_error",
     "santa_version", "santa_release", "santa_samples_per_head", "santa_stream_read",
-    "santa_stream_read_scratch_bytes", "santa_decode_noalloc",
+    "santa_stream_read_scratch_bytes", "santa_decode_noalloc", "santa_status",
 ]
 
 
 class SantaStats(ctypes.Structure):
     _fields_ = [("launches", ctypes.c_int32), ("bytes_k", ctypes.c_int64), ("bytes_v", ctypes.c_int64),
-                ("bytes_qo", ctypes.c_int64), ("unique_rows", ctypes.c_int64)]
+                ("bytes_qo", ctypes.c_int64), ("unique_rows", ctypes.c_int64),
+                ("group_unique_rows", ctypes.POINTER(ctypes.c_int64))]
 
 
 class SantaArgs(ctypes.Structure):
@@ -57,6 +59,7 @@ class SantaArgs(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t), ("idx_out", ctypes.c_void_p), ("prob_out", ctypes.c_void_p),
         ("stats_out", ctypes.POINTER(SantaStats)), ("stage_ms", ctypes.POINTER(ctypes.c_float)),
         ("kt_row_stride", ctypes.c_int64), ("kt_batch_stride", ctypes.c_int64),
+        ("debug_spin_limit", ctypes.c_int32),
     ]
 
 
@@ -84,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.santa_decode_ex.argtypes = [ctypes.POINTER(SantaArgs)]
         L.santa_decode_noalloc.restype = ctypes.c_int
         L.santa_decode_noalloc.argtypes = [ctypes.POINTER(SantaArgs)]
+        L.santa_status.restype = ctypes.c_int
+        L.santa_status.argtypes = [ctypes.POINTER(SantaArgs)]
         L.santa_dense_decode.restype = ctypes.c_int
         L.santa_dense_decode.argtypes = [ctypes.POINTER(SantaArgs)]
         L.santa_samples_per_head.restype = ctypes.c_int64
@@ -221,13 +226,16 @@ def decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="stra
            ternary: bool = False, nk: int | None = None, out: torch.Tensor | None = None,
            workspace: torch.Tensor | None = None, idx_out: torch.Tensor | None = None,
            prob_out: torch.Tensor | None = None, stats: bool = False, stage_ms: bool = False, stream=None,
-           group_bernoulli: int = 0, k_feature_major: bool = False):
+           group_bernoulli: int = 0, k_feature_major: bool = False, multi_launch: bool = False,
+           debug_spin_limit: int = 0):
     """One SANTA / S²ANTA decode step through santa_decode_ex.
 
     k_feature_major: K is K^T [B, Hkv, d, nk] (see feature_major()); group_bernoulli = B > 0 selects the
-    mean-group-query Bernoulli scores with B stratified samples (feature-major K only).
-    Returns out, or (out, info) when stats or stage_ms is requested (info holds the stats fields and the
-    milliseconds [score, chunk CDF + resolve, merge, total] from events between the launches).
+    mean-group-query Bernoulli scores with B stratified samples (feature-major K only); multi_launch forces
+    the multi-launch path; debug_spin_limit > 0 bounds every in-kernel wait to that many polls.
+    Returns out, or (out, info) when stats or stage_ms is requested (info holds the stats fields, the
+    distinct sampled rows per (sequence, KV head) as "group_unique_rows", and the milliseconds [score,
+    chunk CDF + resolve, merge, total] from events between the launches).
     """
     if out is None:
         out = torch.empty_like(q)
@@ -235,10 +243,12 @@ def decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="stra
     _fill_common(a, q, K, V, out, nk, stream, k_feature_major)
     a.S = int(S)
     a.mode = _mode_code(mode, ternary) | (K_FEATURE_MAJOR if k_feature_major else 0)
+    a.mode |= MULTI_LAUNCH if multi_launch else 0
     if group_bernoulli:
         a.mode |= GROUP_BERNOULLI_Q
         a.bern_samples = int(group_bernoulli)
     a.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    a.debug_spin_limit = int(debug_spin_limit)
     need = int(lib().santa_workspace_bytes(a.batch, a.nk, a.heads, a.kv_heads, a.d, a.S, a.mode))
     if workspace is None:
         workspace = new_workspace(need, q.device)
@@ -247,7 +257,9 @@ def decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="stra
     _set_debug_outputs(a, idx_out, prob_out)
     st = SantaStats()
     ms = (ctypes.c_float * 4)()
+    gu = (ctypes.c_int64 * (a.batch * a.kv_heads))()
     if stats:
+        st.group_unique_rows = gu
         a.stats_out = ctypes.pointer(st)
     if stage_ms:
         a.stage_ms = ms
@@ -255,11 +267,27 @@ def decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="stra
     if stats or stage_ms:
         info = {}
         if stats:
-            info.update({f: getattr(st, f) for f, _ in SantaStats._fields_})
+            info.update({f: getattr(st, f) for f, _ in SantaStats._fields_ if f != "group_unique_rows"})
+            info["group_unique_rows"] = [int(x) for x in gu]
         if stage_ms:
             info["stage_ms"] = list(ms)
         return out, info
     return out
+
+
+def status(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="strat", *, workspace=None,
+           nk: int | None = None, stream=None, k_feature_major: bool = False) -> int:
+    """santa_status: the status code the last call with these sizes left in `workspace` (None: the scratch of
+    santa_decode_noalloc). Synchronises the stream. Returns OK or ERR_TIMEOUT (no exception)."""
+    a = SantaArgs()
+    out = torch.empty_like(q)
+    _fill_common(a, q, K, V, out, nk, stream, k_feature_major)
+    a.S = int(S)
+    a.mode = _mode_code(mode, False) | (K_FEATURE_MAJOR if k_feature_major else 0)
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return int(lib().santa_status(ctypes.byref(a)))
 
 
 def decode_noalloc(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, S: int, mode="strat", seed: int = 0, *,

@@ -17,6 +17,15 @@ constexpr int FUSED_CDF_MAX_T = 128;  // up to this many chunks the sampling ker
 // own kernel even for T <= FUSED_CDF_MAX_T: every sampling block would otherwise rebuild all T chunk
 // entries of its heads, fp64 work that then outweighs the extra launch.
 constexpr int64_t SEPARATE_CDF_MIN_BLOCKS = 2048;
+// One-launch decode (score, chunk CDF, sampling, gather and the output sum in one kernel): the blocks of
+// a (KV head, sequence) group meet at barriers in device memory, so every block of the grid must be
+// resident at once (one block per CU). Sizes of the synchronisation region at the start of every
+// workspace, and the largest chunk count per sequence the in-kernel chunk CDF takes (8 chunks per lane).
+constexpr int SYNC_MAX_BLOCKS = 1024;
+constexpr int SYNC_MAX_GROUPS = 1024;
+constexpr int DECODE_MAX_T = 512;
+constexpr int DECODE_MAX_CHUNKS = 16;  // chunks per block: the sampled-key bitmap is scanned by one wave
+constexpr int SPIN_LIMIT_DEFAULT = 1 << 22;  // polls before a bounded wait gives up
 
 // ---------------------------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11):
@@ -274,6 +283,39 @@ __device__ inline void chunk_cdf_wave(const double* m, const double* l, int T, i
   o.last = (int)readlane_f64(wave_incl_max_dpp((double)lp), 63);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Points and the in-chunk search shared by the sampling kernels.
+
+// T_m of point m of query head h in sequence b: i.i.d. u_m, stratified (m + u_m)/S, systematic (m + u)/S
+// with one u per head ("Stochastic Sparse Attention for Memory-Bound Inference", Section 2 Eq. 4 and
+// Section 2.1)
+__device__ inline double point_of(uint64_t seed, int mode, int S, int m, int h, int b, double u_sys) {
+  if (mode == 0) return uniform53(seed, (uint32_t)m, (uint32_t)h, (uint32_t)b, TAG_POINT);
+  if (mode == 1) {
+    const double u = uniform53(seed, (uint32_t)m, (uint32_t)h, (uint32_t)b, TAG_POINT);
+    return ((double)m + u) / (double)S;
+  }
+  return ((double)m + u_sys) / (double)S;
+}
+
+// first j in [0, CHUNK) with P[j] * f > r, else -1 (P nondecreasing; entries past the chunk's last key
+// repeat the chunk total): the half-open inverse-CDF convention 1{F(j-1) <= t < F(j)} (Appendix A.4)
+__device__ inline int search_chunk(const double* P, double f, double r) {
+  int lo = 0, hi = CHUNK;  // answer in [lo, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (P[mid] * f > r) hi = mid; else lo = mid + 1;
+  }
+  return lo < CHUNK ? lo : -1;
+}
+
+// last key of a chunk whose prefix grows (its last key with mass; 0 if none)
+__device__ inline int last_positive(const double* P, int len) {
+  for (int j = len - 1; j > 0; --j)
+    if (P[j] > P[j - 1]) return j;
+  return 0;
+}
+
 // block-wide maximum and sum over NW waves (every thread passes its value; all get the result). The sum
 // is taken in a fixed order: lanes by the DPP scan tree, then the waves in index order. `red` holds NW
 // doubles of LDS; both end with a barrier, so `red` may be reused at once.
@@ -367,6 +409,47 @@ struct Problem {
   bool want_idx;         // the caller asked for idx_out (the fused S²ANTA-flash writes idx only then)
   bool cdf_done;         // the chunk CDF kernel has run: the sampling kernel reads cdf / cscale / lastpos
   uint64_t* bmap;        // [B, Hkv, T, 4, 4] fused S²ANTA-flash: sampled keys of each (chunk, head) as bits
+  int spin_limit;        // polls before a bounded wait gives up (the block then flags itself)
+  int32_t* status;       // [B, Hkv] per call: 0, or 1 if a bounded wait of the group's blocks gave up
+  bool check_sync;       // the merge reads the streaming score blocks' handshake flags (sync_err)
+  // one-launch decode (KM_DECODE): epoch per group, arrival flags and error word per block (grid index
+  // (b * Hkv + kv) * P + r); the per-block partial output sums live in `partial` as [blocks, G, d]
+  uint64_t* sync_epoch;  // [SYNC_MAX_GROUPS]
+  uint64_t* sync_flag_a; // [SYNC_MAX_BLOCKS] chunk statistics published
+  uint64_t* sync_flag_b; // [SYNC_MAX_BLOCKS] partial sums published
+  uint32_t* sync_block_err;  // [SYNC_MAX_BLOCKS]
+  bool one_launch;       // the whole decode runs in the score kernel
 };
+
+// LDS plan of the sampling phase of the one-launch decode for G heads, n chunks per block and T chunks
+// per sequence, inside the `cap` bytes of the score phase's K tiles: per-key 16-bit counts per head, the
+// list and bitmap of the sampled keys, each head's chunk CDF C_0..C_T and chunk scales, and the prefix
+// rows of `nb` chunks per head at a time (nb = 0: does not fit). The same arithmetic on the host (which
+// picks the path) and in the kernel.
+struct DecodeLds {
+  int nb;
+  size_t cnt, list, bits, cdf, scl, rows, total;
+};
+__host__ __device__ inline DecodeLds decode_lds_plan(int G, int n, int T, size_t cap) {
+  const size_t gm = G <= 4 ? 4 : 8, ncw = gm / 2;
+  DecodeLds L;
+  L.cnt = 0;
+  L.list = L.cnt + (size_t)n * CHUNK * ncw * 4;
+  L.bits = L.list + (size_t)n * CHUNK * 4;
+  L.cdf = L.bits + ((size_t)n * CHUNK / 8 + 15) / 16 * 16;
+  L.scl = L.cdf + ((size_t)G * (T + 1) * 8 + 15) / 16 * 16;
+  L.rows = L.scl + (size_t)G * T * 8;
+  const size_t per_chunk = (size_t)G * CHUNK * 8;
+  const size_t want_nb = n < 4 ? (size_t)n : 4;
+  const size_t fit = cap > L.rows ? (cap - L.rows) / per_chunk : 0;
+  L.nb = (int)(fit < want_nb ? fit : want_nb);
+  L.total = L.rows + (size_t)L.nb * per_chunk;
+  return L;
+}
+
+// forms of the streaming score kernel
+constexpr int KM_SCORE = 0;   // scores, statistics and prefix rows for the separate sampling kernel
+constexpr int KM_FLASH = 1;   // S²ANTA-flash kernel 1 fused in
+constexpr int KM_DECODE = 2;  // the whole decode step in one launch
 
 }  // namespace santa

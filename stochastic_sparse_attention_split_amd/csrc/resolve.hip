@@ -35,32 +35,6 @@ constexpr int THREADS = 256;
 static_assert(THREADS == CHUNK, "one thread per key of a chunk in the compaction");
 constexpr int BATCH = 2;   // V rows in flight per lane
 
-__device__ inline double point_of(const Problem& p, int m, int h, int b, double u_sys) {
-  if (p.mode == 0) return uniform53(p.seed, (uint32_t)m, (uint32_t)h, (uint32_t)b, TAG_POINT);
-  if (p.mode == 1) {
-    const double u = uniform53(p.seed, (uint32_t)m, (uint32_t)h, (uint32_t)b, TAG_POINT);
-    return ((double)m + u) / (double)p.S;
-  }
-  return ((double)m + u_sys) / (double)p.S;
-}
-
-// first j in [0, CHUNK) with P[j] * f > r, else -1 (P nondecreasing; entries past the chunk's last key
-// repeat the chunk total)
-__device__ inline int search_chunk(const double* P, double f, double r) {
-  int lo = 0, hi = CHUNK;  // answer in [lo, hi]
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (P[mid] * f > r) hi = mid; else lo = mid + 1;
-  }
-  return lo < CHUNK ? lo : -1;
-}
-
-__device__ inline int last_positive(const double* P, int len) {
-  for (int j = len - 1; j > 0; --j)
-    if (P[j] > P[j - 1]) return j;
-  return 0;
-}
-
 // Compaction of the keys counted in `cnt` (16-bit per-head counts, thread k owns key k), gather of their
 // V rows (each row once for the whole group, count * V into fp32 accumulators), and the chunk's partial
 // sums per head (App. O, Algorithm 5, its value-accumulation step). Ends with every thread past a barrier; `Pt` is reused
@@ -326,7 +300,7 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
       // points falls in this chunk (many chunks hold none): the points are tested first, then found again
       bool any = false;
       for (int c = lane; c < n; c += 64) {
-        const double y = point_of(p, lo + c, h0 + g, b, u_sys) * Z;
+        const double y = point_of(p.seed, p.mode, p.S, lo + c, h0 + g, b, u_sys) * Z;
         any = any || (y < Z ? (c0 <= y && y < c1) : (t == lastc));
       }
       if (__ballot(any) == 0ull) continue;  // wave-uniform
@@ -342,7 +316,7 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
     }
     for (int c = lane; c < n; c += 64) {
       const int m = lo + c;
-      const double y = point_of(p, m, h0 + g, b, u_sys) * Z;
+      const double y = point_of(p.seed, p.mode, p.S, m, h0 + g, b, u_sys) * Z;
       const bool mine = y < Z ? (c0 <= y && y < c1) : (t == lastc);
       if (!mine) continue;
       int j;
@@ -352,6 +326,7 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
       } else {
         j = last_positive(Pt[g], len);
       }
+      j = min(j, len - 1);  // keeps the gather inside the cache even if the score pass flagged a timeout
       p.idx[(bh0 + g) * S + m] = (int32_t)(n0 + j);
       atomicAdd(&cnt[j * CW + (g >> 1)], (g & 1) ? 0x10000u : 1u);
       jpf[hh] = j;
@@ -622,10 +597,10 @@ __global__ __launch_bounds__(THREADS) void resolve_prop_kernel(Problem p) {
       const double ylo = a0 + inv * (tid > 0 ? Pt[g][tid - 1] : 0.0);
       const double yhi = a0 + inv * Pt[g][tid];
       const int lo = (int)floor(ylo), hi = (int)floor(yhi);
-      const int c = hi > lo ? hi - lo : 0;
+      const int c = hi > lo ? min(hi - lo, hS[g]) : 0;
       int32_t* dst = p.idx + (bh0 + g) * p.L + hOff[g];
-      for (int i = 0; i < c; ++i)
-        if (lo + i < hS[g]) dst[lo + i] = (int32_t)(n0 + tid);
+      for (int i = 0; i < c; ++i)  // slots outside the tile's budget are never written
+        if (lo + i >= 0 && lo + i < hS[g]) dst[lo + i] = (int32_t)(n0 + tid);
       w[g >> 1] += (g & 1) ? ((uint32_t)c << 16) : (uint32_t)c;
     }
   }
@@ -633,6 +608,21 @@ __global__ __launch_bounds__(THREADS) void resolve_prop_kernel(Problem p) {
   for (int i = 0; i < NCW; ++i) cnt[tid * CW + i] = w[i];
   __syncthreads();
   chunk_gather<D, BF16, GM>(p, t, kv, b, len, cnt, lkey, lcnt, wsum_i, Pt);
+}
+
+// Whether a bounded wait of the streaming score kernel gave up in one of group grp's blocks (their
+// handshake flags); the merge then writes NaN for the group's heads. `writer` (one block per group)
+// records the outcome in the group's status word, which every call writes. Block-uniform; ends with a
+// barrier.
+__device__ inline bool group_flagged(const Problem& p, int grp, bool writer) {
+  int f = 0;
+  if (p.check_sync) {
+    const int P = p.score_blocks_per_group;
+    for (int i = threadIdx.x; i < P; i += blockDim.x) f |= p.sync_err[(int64_t)grp * P + i];
+  }
+  const bool any = __syncthreads_or(f != 0) != 0;
+  if (writer && threadIdx.x == 0) p.status[grp] = any ? 1 : 0;
+  return any;
 }
 
 // out[b, h] = round((sum over chunks of the partials of head h) / S). One block per (head, sequence, group
@@ -655,6 +645,7 @@ __global__ __launch_bounds__(merge_threads<D>()) void merge_kernel(Problem p) {
   const int tid = threadIdx.x;
   const int G = p.G, T = p.T;
   const int kv = h / G, g = h % G;
+  const bool poisoned = group_flagged(p, b * p.Hkv + kv, g == 0 && blockIdx.z == 0);
   const int c = tid % V4, ts = tid / V4;
   const float* base = p.partial + ((int64_t)(b * p.Hkv + kv) * T * G + g) * D + col0 + 4 * c;
   const int64_t tstride = (int64_t)G * D;
@@ -688,9 +679,9 @@ __global__ __launch_bounds__(merge_threads<D>()) void merge_kernel(Problem p) {
     const double r = tot / (double)p.S;
     const int64_t o = ((int64_t)b * p.H + h) * D + col0 + tid;
     if (BF16)
-      ((uint16_t*)p.out)[o] = f64_to_bf16_rne(r);
+      ((uint16_t*)p.out)[o] = poisoned ? (uint16_t)0x7FC0u : f64_to_bf16_rne(r);
     else
-      ((float*)p.out)[o] = (float)r;
+      ((float*)p.out)[o] = poisoned ? __uint_as_float(0x7FC00000u) : (float)r;
   }
 }
 
@@ -712,6 +703,7 @@ __global__ __launch_bounds__(THREADS) void merge_flash_kernel(Problem p) {
   const int G = p.G, T = p.T;
   const int kv = h / G, g = h % G;
   const int64_t bh = (int64_t)b * p.H + h;
+  const bool poisoned = group_flagged(p, b * p.Hkv + kv, g == 0);
 
   double mx = -INFINITY;
   for (int t = tid; t < T; t += THREADS) mx = fmax(mx, p.cmax[bh * T + t]);
@@ -759,9 +751,9 @@ __global__ __launch_bounds__(THREADS) void merge_flash_kernel(Problem p) {
     const double r = tot / (Z * (double)p.S_tile);
     const int64_t o = bh * D + tid;
     if (BF16)
-      ((uint16_t*)p.out)[o] = f64_to_bf16_rne(r);
+      ((uint16_t*)p.out)[o] = poisoned ? (uint16_t)0x7FC0u : f64_to_bf16_rne(r);
     else
-      ((float*)p.out)[o] = (float)r;
+      ((float*)p.out)[o] = poisoned ? __uint_as_float(0x7FC00000u) : (float)r;
   }
   if (p.fused && p.want_unique && g == 0) {  // distinct sampled keys per chunk: union of the heads' key bits
     const int grp = b * p.Hkv + kv;

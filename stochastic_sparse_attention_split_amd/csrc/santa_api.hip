@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -37,9 +38,14 @@ constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-  size_t stash, cmax, csum, cdf, cscale, lastpos, partial, idx, unique, sink, sync_err, budget, boff, kfeat, bmap,
-      total;
+  size_t sync, status, stash, cmax, csum, cdf, cscale, lastpos, partial, idx, unique, sink, sync_err, budget, boff,
+      kfeat, bmap, total;
 };
+
+// the synchronisation region of the one-launch decode, at offset 0 of every workspace: epochs per group,
+// arrival flags and error words per block
+constexpr size_t SYNC_BYTES =
+    SYNC_MAX_GROUPS * sizeof(uint64_t) + 2 * SYNC_MAX_BLOCKS * sizeof(uint64_t) + SYNC_MAX_BLOCKS * sizeof(uint32_t);
 
 // every region is written by the call before it is read: no initial contents are required
 // sampled keys listed per head: S, or T * S_tile for S²ANTA-flash
@@ -58,6 +64,8 @@ Layout layout(int64_t B, int64_t nk, int64_t H, int64_t Hkv, int64_t d, int64_t 
     off = align_up(off + bytes);
     return at;
   };
+  L.sync = take(SYNC_BYTES);
+  L.status = take((size_t)(B * Hkv) * sizeof(int32_t));
   L.stash = take((size_t)(B * H * T * CHUNK) * sizeof(double));
   L.cmax = take((size_t)(B * H * T) * sizeof(double));
   L.csum = take((size_t)(B * H * T) * sizeof(double));
@@ -117,7 +125,7 @@ int validate_sampled(const santa_args* a, int64_t* seq, int64_t* bstride, int64_
   if (a->S < 1) return fail(SANTA_ERR_INVALID_ARG, "S must be >= 1 (got %d)", a->S);
   const int base = a->mode & 0xFF, flags = a->mode & ~0xFF;
   if (base > SANTA_FLASH || base < 0 ||
-      (flags & ~(SANTA_TERNARY_Q | SANTA_GROUP_BERNOULLI_Q | SANTA_K_FEATURE_MAJOR)))
+      (flags & ~(SANTA_TERNARY_Q | SANTA_GROUP_BERNOULLI_Q | SANTA_K_FEATURE_MAJOR | SANTA_MULTI_LAUNCH)))
     return fail(SANTA_ERR_INVALID_ARG, "mode 0x%x has unknown bits", (unsigned)a->mode);
   if ((flags & SANTA_TERNARY_Q) && (flags & SANTA_GROUP_BERNOULLI_Q))
     return fail(SANTA_ERR_INVALID_ARG, "SANTA_TERNARY_Q and SANTA_GROUP_BERNOULLI_Q exclude each other");
@@ -126,6 +134,7 @@ int validate_sampled(const santa_args* a, int64_t* seq, int64_t* bstride, int64_
   if ((flags & SANTA_GROUP_BERNOULLI_Q) && (a->bern_samples < 1 || a->bern_samples > 64))
     return fail(SANTA_ERR_INVALID_ARG, "bern_samples %d is not in 1..64", a->bern_samples);
   if (a->S > 65535) return fail(SANTA_ERR_UNSUPPORTED, "S %d exceeds 65535", a->S);
+  if (a->debug_spin_limit < 0) return fail(SANTA_ERR_INVALID_ARG, "debug_spin_limit %d < 0", a->debug_spin_limit);
   *kt_row = 0;
   *kt_batch = 0;
   if (flags & SANTA_K_FEATURE_MAJOR) {
@@ -168,6 +177,22 @@ int score_blocks_per_group(int groups, int T, int per_cu) {
   return per < 1 ? 1 : (per > T ? T : per);
 }
 
+// The one-launch decode applies when the streaming score kernel runs (bf16, sequence-major K, G <= 8), the
+// sampling is i.i.d., stratified or systematic, every block of the grid fits on the device at once (one
+// per CU), the chunk CDF fits the in-kernel form and the sampling phase's LDS fits the K tiles. Returns
+// the blocks per group, or 0 when the multi-launch path runs.
+int one_launch_blocks(const Problem& p, int cus) {
+  if (!p.bf16 || p.kfm || p.group_bern || p.mode > SANTA_SYS || p.G > MAX_GROUP || p.T > DECODE_MAX_T) return 0;
+  const int groups = p.B * p.Hkv;
+  if (groups > cus || groups > SYNC_MAX_GROUPS) return 0;
+  const int per = std::min(p.T, cus / groups);
+  if ((int64_t)per * groups > SYNC_MAX_BLOCKS) return 0;
+  const int n = (p.T + per - 1) / per;
+  if (n > DECODE_MAX_CHUNKS || decode_lds_bytes(p.G, n, p.T, p.d) == 0) return 0;
+  if (p.mode == SANTA_IID && (int64_t)n * p.S > 32768) return 0;  // i.i.d. points are tested in every chunk
+  return per;
+}
+
 struct Events {
   hipEvent_t e[4] = {nullptr, nullptr, nullptr, nullptr};
   bool on = false;
@@ -176,6 +201,19 @@ struct Events {
       if (x) (void)hipEventDestroy(x);
   }
 };
+
+// the per-group status words a call leaves in its workspace (stream already synchronised)
+int read_status(const int32_t* status, int batch, int kv_heads) {
+  const int groups = batch * kv_heads;
+  std::vector<int32_t> v((size_t)groups);
+  const hipError_t e = hipMemcpy(v.data(), status, v.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy(status)");
+  for (int g = 0; g < groups; ++g)
+    if (v[g] != 0)
+      return fail(SANTA_ERR_TIMEOUT, "a bounded in-kernel wait gave up for sequence %d, KV head %d; the outputs "
+                  "of its query heads are NaN", g / kv_heads, g % kv_heads);
+  return SANTA_OK;
+}
 
 }  // namespace
 
@@ -252,6 +290,16 @@ int santa_decode_ex(const santa_args* a) {
   p.fused = p.mode == SANTA_FLASH && p.bf16 && p.G <= 4 && !p.kfm;
   p.want_unique = a->stats_out != nullptr;
   p.want_idx = a->idx_out != nullptr;
+  p.spin_limit = a->debug_spin_limit > 0 ? a->debug_spin_limit : SPIN_LIMIT_DEFAULT;
+  p.status = (int32_t*)(ws + L.status);
+  p.check_sync = p.bf16 && !p.kfm;  // the streaming score kernel flags its blocks' handshakes
+  p.sync_epoch = (uint64_t*)(ws + L.sync);
+  p.sync_flag_a = p.sync_epoch + SYNC_MAX_GROUPS;
+  p.sync_flag_b = p.sync_flag_a + SYNC_MAX_BLOCKS;
+  p.sync_block_err = (uint32_t*)(p.sync_flag_b + SYNC_MAX_BLOCKS);
+  const int one = (a->mode & SANTA_MULTI_LAUNCH) ? 0 : one_launch_blocks(p, device_cus());
+  p.one_launch = one > 0;
+  if (p.one_launch) p.score_blocks_per_group = one;
 
   hipStream_t stream = (hipStream_t)a->stream;
   Events ev;
@@ -267,21 +315,25 @@ int santa_decode_ex(const santa_args* a) {
   // with stage timing, HIP records e[0] and e[1] at the score kernel's own start and end
   LaunchEvents sev;
   if (ev.on) sev = LaunchEvents{ev.e[0], ev.e[1]};
-  if ((e = p.kfm ? launch_score_fm(p, stream, sev) : launch_score(p, stream, sev)) != hipSuccess)
+  if (p.one_launch) {
+    if ((e = launch_decode(p, stream, sev)) != hipSuccess) return hip_fail(e, "one-launch decode kernel launch");
+  } else if ((e = p.kfm ? launch_score_fm(p, stream, sev) : launch_score(p, stream, sev)) != hipSuccess) {
     return hip_fail(e, "score kernel launch");
+  }
   const bool prop = p.mode == SANTA_PROP;
   // for T <= FUSED_CDF_MAX_T the sampling kernel builds the chunk CDF (or the prop tile budgets) itself;
   // S²ANTA-flash needs neither
-  const bool cdf_kernel = p.mode != SANTA_FLASH &&
+  const bool cdf_kernel = !p.one_launch && p.mode != SANTA_FLASH &&
                           (p.T > FUSED_CDF_MAX_T ||
                            (!prop && (int64_t)p.B * p.Hkv * p.T > SEPARATE_CDF_MIN_BLOCKS));
   p.cdf_done = cdf_kernel && !prop;
   if (cdf_kernel && !prop && (e = launch_chunk_cdf(p, stream)) != hipSuccess)
     return hip_fail(e, "chunk CDF kernel launch");
   if (cdf_kernel && prop && (e = launch_budget(p, stream)) != hipSuccess) return hip_fail(e, "budget kernel launch");
-  if (!p.fused && (e = launch_resolve(p, stream)) != hipSuccess) return hip_fail(e, "resolve kernel launch");
+  if (!p.one_launch && !p.fused && (e = launch_resolve(p, stream)) != hipSuccess)
+    return hip_fail(e, "resolve kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  if ((e = launch_merge(p, stream)) != hipSuccess) return hip_fail(e, "merge kernel launch");
+  if (!p.one_launch && (e = launch_merge(p, stream)) != hipSuccess) return hip_fail(e, "merge kernel launch");
   if (ev.on && (e = hipEventRecord(ev.e[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
   if (a->stats_out) {
@@ -301,19 +353,19 @@ int santa_decode_ex(const santa_args* a) {
       kbytes = 0;
       for (int32_t x : kf) kbytes += (int64_t)x * a->nk * esz;
     }
-    if (!p.kfm && p.bf16) {  // the streaming score kernel flags a timed-out LDS handshake per block
-      std::vector<int32_t> fl((size_t)p.score_blocks_per_group * p.Hkv * p.B);
-      if ((e = hipMemcpy(fl.data(), p.sync_err, fl.size() * sizeof(int32_t), hipMemcpyDeviceToHost)) != hipSuccess)
-        return hip_fail(e, "hipMemcpy(sync flags)");
-      for (int32_t x : fl)
-        if (x != 0) return fail(SANTA_ERR_HIP, "score kernel: an LDS handshake timed out (%d)", x);
-    }
     santa_stats* s = a->stats_out;
-    s->launches = p.fused ? 2 : (cdf_kernel ? 4 : 3);
+    s->launches = p.one_launch ? 1 : (p.fused ? 2 : (cdf_kernel ? 4 : 3));
     s->bytes_k = kbytes;
     s->bytes_v = U * a->d * esz;
     s->bytes_qo = 2 * (int64_t)a->batch * a->heads * a->d * esz;
     s->unique_rows = U;
+    if (s->group_unique_rows)
+      for (int g = 0; g < a->batch * a->kv_heads; ++g) {
+        int64_t ug = 0;
+        for (int t = 0; t < p.T; ++t) ug += u[(size_t)g * p.T + t];
+        s->group_unique_rows[g] = ug;
+      }
+    if ((st = read_status(p.status, a->batch, a->kv_heads)) != SANTA_OK) return st;
   }
   if (ev.on) {
     if ((e = hipEventSynchronize(ev.e[3])) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
@@ -433,6 +485,29 @@ int santa_decode_noalloc(const santa_args* a) {
   return santa_decode_ex(&b);
 }
 
+int santa_status(const santa_args* a) {
+  g_err.clear();
+  if (!a) return fail(SANTA_ERR_INVALID_ARG, "args is NULL");
+  int64_t seq = 0, bstride = 0, kt_row = 0, kt_batch = 0;
+  santa_args b = *a;
+  const void* ws = a->workspace;
+  int st;
+  if (!ws) {  // santa_decode_noalloc's scratch of the current device
+    void* ptr = nullptr;
+    if ((st = scratch_address(&ptr))) return st;
+    b.workspace = ptr;
+    b.workspace_bytes = SANTA_NOALLOC_MAX_BYTES;
+  }
+  if ((st = validate_sampled(&b, &seq, &bstride, &kt_row, &kt_batch))) return st;
+  const Layout L = layout(b.batch, b.nk, b.heads, b.kv_heads, b.d, b.S, b.mode);
+  if (b.workspace_bytes < L.total)
+    return fail(SANTA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", b.workspace_bytes,
+                L.total);
+  const hipError_t e = hipStreamSynchronize((hipStream_t)b.stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  return read_status((const int32_t*)((const char*)b.workspace + L.status), b.batch, b.kv_heads);
+}
+
 void santa_release(void) {
   std::lock_guard<std::mutex> lock(g_ws_mu);
   int cur = 0;
@@ -523,6 +598,7 @@ const char* santa_status_string(int status) {
     case SANTA_ERR_UNSUPPORTED: return "unsupported configuration";
     case SANTA_ERR_WORKSPACE: return "workspace too small";
     case SANTA_ERR_HIP: return "HIP runtime error";
+    case SANTA_ERR_TIMEOUT: return "a bounded in-kernel wait gave up";
     default: return "unknown status";
   }
 }

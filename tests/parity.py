@@ -145,6 +145,9 @@ def compare(q, K, V, S, mode: str, seed: int, *, ternary=False, dtype="bf16", wa
     if not nmis:
         Ug = int(info["unique_rows"])
         assert Ug == int(r.unique.sum()), f"{label}: unique rows {Ug} != oracle {int(r.unique.sum())}"
+        assert info["group_unique_rows"] == [int(x) for x in np.asarray(r.unique).reshape(-1)], \
+            f"{label}: distinct rows per (sequence, KV head) differ from the oracle's"
+    assert sum(info["group_unique_rows"]) == info["unique_rows"]
     esz = 2 if dtype == "bf16" else 4
     if kfm:
         rows = _feature_rows(qn, Kn, seed, ternary, group_b, gcounts)

@@ -230,8 +230,10 @@ def test_flash_workload_2(S):
 @pytest.mark.parametrize("mode,S", [("strat", 256), ("prop", 128), ("flash", 2048)])
 def test_head_parallel_share_of_workload_2(mode, S):
     """One GPU's share of an 8-way head-parallel split of the 32k Llama-3.1-8B-shaped layer: the first KV
-    group and its 4 query heads in a cache of their own. Against the oracle, and bit-identical to the same
-    heads of the whole-layer call: every kernel is local to a (sequence, KV group) unit."""
+    group and its 4 query heads in a cache of their own. Against the oracle, with indices identical to the
+    same heads of the whole-layer call (every kernel is local to a (sequence, KV group) unit); the outputs
+    agree to the parity tolerance (the one-launch decode groups its fp32 partial sums by the blocks of the
+    launch, and the share runs on more blocks per group)."""
     w = workloads.make(2)
     G = w.H // w.Hkv
     q8 = w.q[:, :G].contiguous()
@@ -245,8 +247,8 @@ def test_head_parallel_share_of_workload_2(mode, S):
     L = santa.samples_per_head(w.nk, S, mode)
     idx = torch.empty((w.B, w.H, L), dtype=torch.int32, device=dev)
     out = santa.decode(w.q.to(dev), w.K.to(dev), w.V.to(dev), S, mode, w.seed, idx_out=idx)
-    assert torch.equal(out[:, :G].cpu(), out8.cpu())
     assert torch.equal(idx[:, :G].cpu(), idx8.cpu())
+    assert float((out[:, :G].float() - out8.float()).abs().max()) <= 2e-2
 
 
 FM_CASES = [
@@ -531,3 +533,66 @@ def test_stream_read_probe_reads_every_byte():
         log(f"stream read {n * 4} bytes: xor {got:#010x} want {want:#010x}")
         assert got == want
 
+
+
+ONE_LAUNCH_CASES = [
+    # B, H, Hkv, d, nk, mode, S, ternary, spikes: shapes the one-launch decode takes
+    (1, 32, 8, 128, 32768, "strat", 256, False, 32),   # the benchmark workload: 32 blocks per group, 4 chunks each
+    (1, 4, 1, 128, 30000, "sys", 128, False, 8),       # 118 chunks, one chunk per block
+    (2, 16, 2, 128, 60000, "iid", 64, False, 6),       # 4 groups, 235 chunks: prefix rows in memory
+    (1, 28, 4, 128, 131072, "strat", 512, False, 40),  # G = 7, 512 chunks, 8 per block
+    (3, 16, 8, 64, 25563, "strat", 64, True, 2),       # 24 groups, 10 chunks per block, ragged tail, ternary
+    (1, 6, 2, 64, 777, "sys", 5, False, 1),            # 4 chunks, G = 3
+]
+
+
+@pytest.mark.parametrize("case", ONE_LAUNCH_CASES,
+                         ids=[f"B{c[0]}H{c[1]}kv{c[2]}d{c[3]}n{c[4]}{c[5]}S{c[6]}" for c in ONE_LAUNCH_CASES])
+def test_one_launch_matches_multi_launch(case):
+    """The one-launch decode (one kernel) and the multi-launch path (score, sampling, merge kernels) take
+    the same indices; their outputs differ only in the grouping of the fp32 partial sums."""
+    B, H, Hkv, d, nk, mode, S, tern, spikes = case
+    log(f"one launch vs multi launch {case}")
+    dev = torch.device("cuda:0")
+    q, K, V, _ = workloads.make_inputs(B, H, Hkv, d, nk, dtype="bf16", spikes_per_head=spikes,
+                                       rng_seed=zlib.crc32(repr(case).encode()) & 0xFFFF)
+    qd, Kd, Vd = q.to(dev), K.to(dev), V.to(dev)
+    i1 = torch.empty((B, H, S), dtype=torch.int32, device=dev)
+    i2 = torch.empty_like(i1)
+    o1, info1 = santa.decode(qd, Kd, Vd, S, mode, 3, ternary=tern, idx_out=i1, stats=True)
+    o2, info2 = santa.decode(qd, Kd, Vd, S, mode, 3, ternary=tern, idx_out=i2, stats=True, multi_launch=True)
+    torch.cuda.synchronize()
+    log(f"  launches {info1['launches']} vs {info2['launches']}, unique rows {info1['unique_rows']}")
+    assert info1["launches"] == 1 and info2["launches"] >= 3
+    assert torch.equal(i1, i2)
+    assert info1["group_unique_rows"] == info2["group_unique_rows"]
+    assert float((o1.float() - o2.float()).abs().max()) <= 2e-2
+
+
+@pytest.mark.parametrize("mode,multi", [("strat", False), ("sys", True), ("flash", False)])
+def test_bounded_wait_timeout_poisons_outputs_and_reports(mode, multi):
+    """A spin limit of one poll makes the kernels' own bounded waits give up (every kernel still exits
+    normally): the affected heads' outputs are NaN, santa_status and the stats path report
+    SANTA_ERR_TIMEOUT, and the next call with the default limit is correct again."""
+    log(f"bounded-wait timeout path: {mode}, multi-launch {multi}")
+    dev = torch.device("cuda:0")
+    q, K, V, _ = workloads.make_inputs(1, 8, 2, 128, 20000, dtype="bf16", spikes_per_head=4, rng_seed=88)
+    qd, Kd, Vd = q.to(dev), K.to(dev), V.to(dev)
+    S = 64
+    ws = santa.new_workspace(santa.workspace_bytes(1, 20000, 8, 2, 128, S, mode), dev)
+    ref = santa.decode(qd, Kd, Vd, S, mode, 4, workspace=ws, multi_launch=multi)
+    assert santa.status(qd, Kd, Vd, S, mode, workspace=ws) == santa.OK
+    bad = santa.decode(qd, Kd, Vd, S, mode, 4, workspace=ws, multi_launch=multi, debug_spin_limit=1)
+    torch.cuda.synchronize()
+    assert santa.status(qd, Kd, Vd, S, mode, workspace=ws) == santa.ERR_TIMEOUT
+    nan_heads = int(torch.isnan(bad.float()).all(dim=-1).sum())
+    log(f"  {nan_heads} of 8 heads NaN")
+    assert nan_heads >= 1
+    assert bool(torch.isnan(bad.float()).any(dim=-1).eq(torch.isnan(bad.float()).all(dim=-1)).all())
+    with pytest.raises(santa.SantaError) as exc:
+        santa.decode(qd, Kd, Vd, S, mode, 4, workspace=ws, multi_launch=multi, debug_spin_limit=1, stats=True)
+    assert exc.value.status == santa.ERR_TIMEOUT
+    again = santa.decode(qd, Kd, Vd, S, mode, 4, workspace=ws, multi_launch=multi)
+    torch.cuda.synchronize()
+    assert santa.status(qd, Kd, Vd, S, mode, workspace=ws) == santa.OK
+    assert torch.equal(again, ref)
