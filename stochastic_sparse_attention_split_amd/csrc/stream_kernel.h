@@ -1,4 +1,4 @@
-// Streaming score pass for bf16 caches: one block of 12 waves per CU with copy, matrix-core and
+// Streaming score pass for bf16 caches: one block of 16 waves per CU with copy, matrix-core and
 // exponential roles (described above score_stream_kernel). Three forms share it:
 //   KM_SCORE:  scores, chunk statistics and the in-chunk prefix rows ("stash") for the sampling kernel;
 //   KM_FLASH:  S²ANTA-flash kernel 1 fused in (samples and gathers each tile right after its exponentials);
@@ -25,11 +25,11 @@ __device__ inline double piece_elem(const uint4& w, int e) {
   }
 }
 
-// Streaming form for bf16 caches (one block per CU). The memory system copies each chunk's K tile
-// straight into LDS (global_load_lds: 16 bytes per lane, no register staging), two tiles in flight: the
-// copy of chunk k+2 starts as soon as chunk k's matrix-core pass has finished reading its tile, so the
-// HBM stream does not pause for the exponentials and stores. The compiler does not track these copies;
-// the block waits for them with explicit vmcnt waits whose counts are derived in the loop below.
+// Streaming form for bf16 caches (one block per CU). The memory system copies K straight into LDS
+// (global_load_lds: 16 bytes per lane, no register staging) in half-chunk buffers, two chunks in flight:
+// the copy of a buffer's next half-chunk starts as soon as the matrix waves have finished reading it, so
+// the HBM stream does not pause for the exponentials and stores. The compiler does not track these
+// copies; the copy waves wait for them with explicit vmcnt waits.
 
 // the LDS address of a __shared__ object, as the 32-bit offset M0 takes
 __device__ inline uint32_t lds_addr(const void* ptr) {
@@ -59,17 +59,20 @@ __device__ inline void wait_vm() {
   else static_assert(N == 0, "unsupported count");
 }
 
-constexpr int SQUART = 4;                // key quarters of a chunk (64 keys each): one matrix wave each
+constexpr int SQUART = 8;                // matrix waves: four per half of a chunk (32 keys each), two per SIMD
 constexpr int SSOFT = 4;                 // exponential waves: one head each (two for G = 5..8)
-constexpr int SCOPY = 4;                 // copy waves: two per K tile
-constexpr int STHREADS = 64 * (SQUART + SSOFT + SCOPY);  // 12 waves: three per SIMD
+constexpr int SCOPY = 4;                 // copy waves: one per half-chunk K buffer
+constexpr int NBUF = 4;                  // half-chunk K buffers in LDS (two chunks in flight)
+constexpr int HALF = CHUNK / 2;          // keys per buffer
+constexpr int SPH = SQUART / 2;          // matrix waves per half
+constexpr int STHREADS = 64 * (SQUART + SSOFT + SCOPY);  // 16 waves: four per SIMD
 
 template <int D>
 struct SGeo {
   static constexpr int ROWB = D * 2;         // bytes per bf16 K row
   static constexpr int PPR = ROWB / 16;      // 16-byte pieces per row (16 or 8)
-  static constexpr int TILE = CHUNK * ROWB;  // bytes per chunk tile (64 or 32 KiB)
-  static constexpr int CPW = TILE / 1024 / 2;  // wave-wide 1 KiB copies per copy wave per chunk (32 or 16)
+  static constexpr int HTILE = HALF * ROWB;  // bytes per half-chunk buffer (32 or 16 KiB)
+  static constexpr int CPH = HTILE / 1024;   // wave-wide 1 KiB copies per half chunk (32 or 16)
   static constexpr int RPS = 1024 / ROWB;    // rows per 1 KiB copy (4 or 8)
   static constexpr int PP = PPR / 4;         // pieces per lane per row in the matrix-core layout
   static constexpr int PPH = PP / 2;         // of which one half of the head dimension holds
@@ -165,28 +168,28 @@ __device__ inline bool wait_ge(int* ctr, int target, int limit) {
   return true;
 }
 
-// Streaming score pass for bf16 caches and G <= 8, one block of 12 waves per CU (one wave of each role
-// per SIMD), three roles that meet only through LDS counters (no block-wide barrier after the start), so
-// the K stream, the matrix cores and the exponentials overlap:
-//   * waves 0..3: fp64 MFMA over key quarter w (64 keys: four 16-key groups) and the whole head dimension
-//     (element parity gives eight independent accumulation chains per head group), writing complete
-//     scores. Two half-row waves per SIMD keep the matrix pipe busier on their own, but beside the K
-//     stream writing into LDS one whole-row wave is no slower, and no partial rows need adding. For
-//     G = 5..8 (HG = 2) the wave scores both head groups: each K element is converted once for the
+// Streaming score pass for bf16 caches and G <= 8, one block of 16 waves per CU (four per SIMD), three
+// roles that meet only through LDS counters (no block-wide barrier after the start), so the K stream, the
+// matrix cores and the exponentials overlap:
+//   * waves 0..7: fp64 MFMA, two per SIMD: waves 0..3 score the first half of every chunk, waves 4..7 the
+//     second (32 keys each: two 16-key groups) over the whole head dimension (element parity gives four
+//     independent accumulation chains per head group), writing complete scores. Two matrix waves per SIMD
+//     keep the fp64 matrix pipe busier than one (one wave alone issues an MFMA only every ~46 cycles).
+//     For G = 5..8 (HG = 2) the wave scores both head groups: each K element is converted once for the
 //     MFMAs of the eight heads, and the query operands are read from LDS per 4-piece step to stay within
-//     the register budget of three waves per SIMD;
-//   * waves 4..7: chunk max, exponentials, in-chunk prefix and the stores of head w - 4 (and w for
+//     the register budget of four waves per SIMD;
+//   * waves 8..11: chunk max, exponentials, in-chunk prefix and the stores of head w - 8 (and w - 4 for
 //     G = 5..8);
-//   * waves 8..11: global -> LDS copies (global_load_lds) of the K tiles, waves 8-9 tile 0 with the
-//     block's even chunks, 10-11 tile 1 with the odd ones (wave 10 first copies the queries). The first
-//     chunk of tile 1 is requested only once tile 0 has landed, so across the device the first tiles
-//     arrive before any second one and the matrix cores start half a pass earlier.
-// Counters (chunk k lives in tile k & 1; its fill index there is k >> 1):
-//   ld[j] +1 per copy wave when its half of tile j's current chunk has landed;
-//   use[j] +1 per MFMA wave when its reads of tile j are done;  pr +1 per MFMA wave per chunk whose
-//   scores are written;  pc +1 per exponential wave per chunk whose scores it has read;  qr queries
-//   landed;  pb prologue barrier;  fin waves finished (the last one publishes the block's handshake
-//   status).
+//   * waves 12..15: global -> LDS copies (global_load_lds) into four half-chunk K buffers: copy wave j
+//     fills buffer j with half (j & 1) of the block's chunks (j >> 1), (j >> 1) + 2, ... (wave 15 first
+//     copies the queries). Half-chunk buffers are released as soon as their half is scored, so the next
+//     copy starts half a chunk earlier than with whole-chunk tiles. The block's second chunk is requested
+//     only once its first has landed, so across the device the first chunks arrive before any second one.
+// Counters (chunk k's half h lives in buffer 2 (k & 1) + h; its fill index there is k >> 1):
+//   ld[j] +1 when buffer j's current half-chunk has landed;  use[j] +1 per MFMA wave when its reads of
+//   buffer j are done;  pr +1 per MFMA wave per chunk whose scores are written;  pc +1 per exponential
+//   wave per chunk whose scores it has read;  qr queries landed;  pb prologue barrier;  fin waves finished
+//   (the last one publishes the block's handshake status).
 // HG = head groups of four (G <= 4 * HG).
 // FL: S²ANTA-flash kernel 1 ("Stochastic Sparse Attention for Memory-Bound Inference", Section 3.3 and
 // Appendix P, Algorithm 7) fused in: right after a chunk's exponentials, the exponential wave of head g
@@ -220,29 +223,29 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   constexpr int NMF = SQUART;  // matrix-core waves
   constexpr int NTH = 64 * (NMF + SSOFT + SCOPY);
   using Sg = SGeo<D>;
-  constexpr int EPL = 8, PPH = Sg::PPH, CPW = Sg::CPW;
-  constexpr int KPW = CHUNK / SQUART;  // keys per MFMA wave
+  constexpr int EPL = 8, PPH = Sg::PPH, CPH = Sg::CPH;
+  constexpr int KPW = HALF / SPH;     // keys per MFMA wave
   constexpr int NGR = KPW / 16;       // 16-key groups per MFMA wave
   constexpr int HM = 4 * HG;          // heads held
   constexpr int NPW = 2 * PPH;       // 4-piece steps of a row per MFMA wave
   static_assert(D * 2 * HM <= 1024 * HG, "the queries of a group fit HG 1 KiB copies");
 
-  __shared__ __align__(16) unsigned char kt[2][Sg::TILE];
+  __shared__ __align__(16) unsigned char kt[NBUF][Sg::HTILE];
   __shared__ __align__(16) double part[HG][4][CHUNK];  // scores: [head group][head][key]
   __shared__ __align__(16) double qe[HM][D + 2];
   __shared__ double hnorm[HM];
   __shared__ __align__(16) unsigned char qs[1024 * HG];
   __shared__ int rl[FL ? 4 : 1][FL ? CHUNK : 1];  // fused S²ANTA-flash: sampled rows (key | count << 8) per head
-  constexpr int NCTR = 10;
+  constexpr int NCTR = 14;
   __shared__ int ctr[NCTR];
-  int* ld = &ctr[0];   // [2]
-  int* use = &ctr[2];  // [2]
-  int* pr = &ctr[4];
-  int* pc = &ctr[5];
-  int* qr = &ctr[6];
-  int* pb = &ctr[7];
-  int* fin = &ctr[8];
-  int* bad = &ctr[9];
+  int* ld = &ctr[0];   // [NBUF]
+  int* use = &ctr[4];  // [NBUF]
+  int* pr = &ctr[8];
+  int* pc = &ctr[9];
+  int* qr = &ctr[10];
+  int* pb = &ctr[11];
+  int* fin = &ctr[12];
+  int* bad = &ctr[13];
   __shared__ int dstat[2];      // one-launch decode: barrier outcomes (0 = passed)
   __shared__ int wcnt[STHREADS / 64];
   uint64_t epoch = 0;           // one-launch decode: the group's epoch, read by the polling wave at its start
@@ -278,16 +281,17 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   };
 
   if (wave >= NMF + SSOFT) {
-    // ---- copy waves: at most one chunk's copies in flight per wave, so vmcnt(0) means all landed.
-    // Highest issue priority on their SIMD: they issue rarely and the whole block waits on them.
+    // ---- copy waves: copy wave j fills buffer j with half (j & 1) of the block's chunks k = (j >> 1),
+    // (j >> 1) + 2, ...; at most one half-chunk's copies in flight per wave, so vmcnt(0) means all
+    // landed. Highest issue priority on their SIMD: they issue rarely and the whole block waits on them.
     __builtin_amdgcn_s_setprio(3);
-    const int j = (wave - NMF - SSOFT) >> 1, hf = (wave - NMF - SSOFT) & 1;
+    const int j = wave - NMF - SSOFT, hh = j & 1;
     // every block reads its group's epoch before it can publish anything; it changes only after every
     // block of the group has published its partial sums (see decode_tail)
     if constexpr (DEC)
       if (wave == NMF + SSOFT)
         epoch = __hip_atomic_load(p.sync_epoch + b * p.Hkv + kv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (j == 1 && hf == 0) {
+    if (j == SCOPY - 1) {
       const char* qsrc = (const char*)p.q + ((int64_t)b * p.H + h0) * D * 2;
 #pragma unroll
       for (int c = 0; c < HG; ++c)  // bytes past the group's queries re-read its last piece (never used)
@@ -295,21 +299,21 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
       wait_vm<0>();
       signal(qr, lane);
     }
-    for (int k = j, m = 0; k < n && ok; k += 2, ++m) {
-      if (m > 0) ok = wait_ge(&use[j], NMF * m, p.spin_limit);  // the tile's previous chunk is no longer read
-      if (m == 0 && j == 1) ok = wait_ge(&ld[0], 2, p.spin_limit);  // the block's first chunk goes first
+    for (int k = j >> 1, m = 0; k < n && ok; k += 2, ++m) {
+      if (m > 0) ok = wait_ge(&use[j], SPH * m, p.spin_limit);  // the buffer's previous half is no longer read
+      // the block's second chunk is requested once the same half of its first has landed, so across the
+      // device every block's first chunk arrives before any second one
+      if (m == 0 && j >= 2) ok = wait_ge(&ld[j - 2], 1, p.spin_limit);
       if (!ok) break;
       const int t = t0 + k * step;
-      const int64_t n0 = (int64_t)t * CHUNK;
-      const int len = chunk_len(t);
+      const int64_t c0 = (int64_t)t * CHUNK, h0k = c0 + hh * HALF;
       const uint32_t base = lds_addr(&kt[j][0]);
 #pragma unroll 4
-      for (int i = 0; i < CPW; ++i) {
-        const int q = hf * CPW + i;
-        const int row = q * Sg::RPS + lane / Sg::PPR;
+      for (int i = 0; i < CPH; ++i) {
+        const int row = i * Sg::RPS + lane / Sg::PPR;  // row of the half
         const int pc = (lane % Sg::PPR) ^ (row % Sg::PPR);
-        const int grow = row < len ? row : 0;  // rows past the end re-read row 0 (masked later)
-        copy_to_lds16(kbase + (n0 + grow) * seq_bytes + pc * 16, base + q * 1024);
+        const int64_t key = h0k + row < p.nk ? h0k + row : c0;  // keys past the end re-read the chunk's first
+        copy_to_lds16(kbase + key * seq_bytes + pc * 16, base + i * 1024);
       }
       wait_vm<0>();
       signal(&ld[j], lane);
@@ -319,7 +323,7 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   }
 
   {
-  // ---- prologue of the MFMA and exponential waves (12 waves, counter barrier pb)
+  // ---- prologue of the MFMA and exponential waves (counter barrier pb)
   int np = 0;
   auto pbar = [&]() {
     signal(pb, lane);
@@ -583,12 +587,13 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
 
   // ---- MFMA waves: 16-key groups x element parity = independent accumulation chains
   const int slot = lane >> 4;
+  const int mh = wave / SPH, quart = wave % SPH;  // this wave's half of each chunk and key slice in it
   if constexpr (HG == 2) {
-    const int quart = wave;
     for (int k = 0; k < n && ok; ++k) {
-      ok = wait_ge(&ld[k & 1], 2 * ((k >> 1) + 1), p.spin_limit);  // chunk k's tile has landed
+      const int jb = 2 * (k & 1) + mh;
+      ok = wait_ge(&ld[jb], (k >> 1) + 1, p.spin_limit);  // chunk k's half has landed
       if (!ok) break;
-      const unsigned char* ks = &kt[k & 1][0];
+      const unsigned char* ks = &kt[jb][0];
       double acc[HG][NGR][2];  // [head group][key group][element parity]
 #pragma unroll
       for (int hx = 0; hx < HG; ++hx)
@@ -615,22 +620,21 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
               acc[hx][gi][e & 1] = __builtin_amdgcn_mfma_f64_4x4x4f64(a, qv[hx][e], acc[hx][gi][e & 1], 0, 0, 0);
           }
       }
-      signal(&use[k & 1], lane);  // this wave's reads of tile k & 1 are complete
+      signal(&use[jb], lane);  // this wave's reads of the buffer are complete
       if (k >= 1) ok = wait_ge(pc, SSOFT * k, p.spin_limit);  // chunk k - 1's partials were read
       if (!ok) break;
 #pragma unroll
       for (int hx = 0; hx < HG; ++hx)
 #pragma unroll
         for (int gi = 0; gi < NGR; ++gi) {
-          const int key = quart * KPW + gi * 16 + 4 * ((lane >> 2) & 3) + (lane >> 4);
+          const int key = mh * HALF + quart * KPW + gi * 16 + 4 * ((lane >> 2) & 3) + (lane >> 4);
           part[hx][lane & 3][key] = acc[hx][gi][0] + acc[hx][gi][1];
         }
       signal(pr, lane);
     }
     SK_PHASE1_DONE();
   }
-  // key quarter over the whole head dimension (HG = 1)
-  const int quart = wave;
+  // key slice over the whole head dimension (HG = 1)
   const int qrow = lane & 3;
   double qb[NPW][EPL];
 #pragma unroll
@@ -638,9 +642,10 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qb[pp][e] = qe[qrow][EPL * (4 * pp + slot) + e];
   for (int k = 0; k < n && ok; ++k) {
-    ok = wait_ge(&ld[k & 1], 2 * ((k >> 1) + 1), p.spin_limit);  // chunk k's tile has landed
+    const int jb = 2 * (k & 1) + mh;
+    ok = wait_ge(&ld[jb], (k >> 1) + 1, p.spin_limit);  // chunk k's half has landed
     if (!ok) break;
-    const unsigned char* ks = &kt[k & 1][0];
+    const unsigned char* ks = &kt[jb][0];
     double acc[NGR][2];  // [group][element parity]
 #pragma unroll
     for (int gi = 0; gi < NGR; ++gi) acc[gi][0] = acc[gi][1] = 0.0;
@@ -657,12 +662,12 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
           acc[gi][e & 1] = __builtin_amdgcn_mfma_f64_4x4x4f64(piece_elem<true>(a4[gi], e), qb[pp][e],
                                                                acc[gi][e & 1], 0, 0, 0);
     }
-    signal(&use[k & 1], lane);  // this wave's reads of tile k & 1 are complete
+    signal(&use[jb], lane);  // this wave's reads of the buffer are complete
     if (k >= 1) ok = wait_ge(pc, SSOFT * k, p.spin_limit);  // chunk k - 1's partials were read
     if (!ok) break;
 #pragma unroll
     for (int gi = 0; gi < NGR; ++gi) {
-      const int key = quart * KPW + gi * 16 + 4 * ((lane >> 2) & 3) + (lane >> 4);
+      const int key = mh * HALF + quart * KPW + gi * 16 + 4 * ((lane >> 2) & 3) + (lane >> 4);
       part[0][lane & 3][key] = acc[gi][0] + acc[gi][1];
     }
     signal(pr, lane);
@@ -709,7 +714,7 @@ decode_tail: __attribute__((unused));
     const int nbits = (n * CHUNK + 31) / 32;
     for (int i = tid; i < n * CHUNK * NCW; i += STHREADS) cnt[i] = 0u;
     for (int i = tid; i < nbits; i += STHREADS) bits[i] = 0u;
-    // the head of this wave: the exponential waves take heads 0..3, the MFMA waves heads 4..7
+    // the head of this wave: the exponential waves take heads 0..3, MFMA waves 0..3 heads 4..7
     const int hw = (wave >= NMF && wave < NMF + SSOFT) ? wave - NMF : ((HG == 2 && wave < NMF) ? wave + 4 : -1);
     const bool headwave = hw >= 0 && hw < G;
     const int64_t bhw = (int64_t)b * p.H + h0 + (headwave ? hw : 0);
