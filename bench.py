@@ -63,13 +63,26 @@ def source_hash(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_record(kernel_src: str):
-    """Measured HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
-    p = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
+KERNEL_SOURCES = ("stochastic_sparse_attention_split_amd/csrc/stream_kernel.h",
+                  "stochastic_sparse_attention_split_amd/csrc/fused.hip",
+                  "stochastic_sparse_attention_split_amd/csrc/common.h")
+
+
+def sources_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record():
+    """Measured HBM bytes per launch of the one-launch decode kernel from committed rocprofv3 counter runs,
+    if its sources are unchanged since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
-    if rec.get("source_sha256_16") != source_hash(kernel_src):
+    if rec.get("sources_sha256_16") != sources_hash():
         return None
     return rec.get("bytes_per_launch")
 
@@ -271,12 +284,16 @@ def main():
         tp["speedup_vs_dense"] = round(tp["dense_bf16_us_median"] / tp["us_median"], 3)
         del q8, K8, V8, ws8, dws8
 
-    # the device's streaming read rate on the same K bytes under the same cold protocol: the practical
-    # ceiling of the score pass's HBM stream, beside the published peak
+    # the device's streaming read rate on the same K bytes under the same cold protocol, timed like the
+    # decode kernel (events at the kernel's own start and end): the practical ceiling of the K stream,
+    # beside the published peak
     rscratch = torch.empty(int(santa.lib().santa_stream_read_scratch_bytes()), dtype=torch.uint8, device=dev)
     for _ in range(args.warmup):
         santa.stream_read(K, rscratch, stream)
-    read_us = timed(lambda: santa.stream_read(K, rscratch, stream), args.steps, cold=True)
+    read_us = []
+    for _ in range(args.steps):
+        thrash.add_(1.0)
+        read_us.append(santa.stream_read(K, rscratch, stream, kernel_time=True)[1] * 1e3)
     read_GBps = K.numel() * K.element_size() / (statistics.median(read_us) * 1e-6) / 1e9
 
     dense_us = None
@@ -289,10 +306,16 @@ def main():
     mean = statistics.fmean(us)
     esz = 2 if w.dtype == "bf16" else 4
     alg_bytes = info["bytes_k"] + info["bytes_v"] + info["bytes_qo"]
-    score_bytes = info["bytes_k"] + w.B * w.H * w.d * esz
-    achieved = score_bytes / (score_us * 1e-6) / 1e9
-    kernel_src = os.path.join(ROOT, "stochastic_sparse_attention_split_amd", "csrc", "score.hip")
-    traffic = traffic_record(kernel_src)
+    one_launch = int(info["launches"]) == 1
+    if one_launch:  # the one kernel is the whole step: its algorithmic bytes are the step's
+        kernel_name = "one-launch decode (score, chunk CDF, sampling, gather, output sum)"
+        kernel_bytes = alg_bytes
+        traffic = traffic_record()
+    else:
+        kernel_name = "score (split-K fp64 MFMA scores + chunk max/sum-exp + in-chunk prefix)"
+        kernel_bytes = info["bytes_k"] + w.B * w.H * w.d * esz
+        traffic = None
+    achieved = kernel_bytes / (score_us * 1e-6) / 1e9
 
     res = {
         "metric": METRIC,
@@ -325,21 +348,26 @@ def main():
         "us_min": round(min(us), 3),
         "us_warm_median": round(statistics.median(us_warm), 3),
         "us_graph_replay_median": round(statistics.median(us_graph), 3) if us_graph else None,
-        "stage_us_mean": {"score": round(score_us, 3), "cdf_resolve": round(float(np.mean(stage[:, 1])), 3),
-                          "merge": round(float(np.mean(stage[:, 2])), 3),
-                          "total_with_events": round(float(np.mean(stage[:, 3])), 3)},
+        "stage_us_mean": ({"decode_kernel": round(score_us, 3),
+                           "total_with_events": round(float(np.mean(stage[:, 3])), 3)} if one_launch else
+                          {"score": round(score_us, 3), "cdf_resolve": round(float(np.mean(stage[:, 1])), 3),
+                           "merge": round(float(np.mean(stage[:, 2])), 3),
+                           "total_with_events": round(float(np.mean(stage[:, 3])), 3)}),
         "roofline": {
-            "kernel": "score (split-K fp64 MFMA scores + chunk max/sum-exp + in-chunk prefix)",
+            "kernel": kernel_name,
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
+            "traffic_over_algorithmic": round(traffic / kernel_bytes, 4) if traffic else None,
+            "kernel_us_mean": round(score_us, 3),
+            "algorithmic_bytes": int(kernel_bytes),
             "measured_read_peak": round(read_GBps, 1),
             "frac_of_measured_read_peak": round(achieved / read_GBps, 4),
         },
-        "stream_read_K": {"bytes": int(K.numel() * K.element_size()), "us_median": round(statistics.median(read_us), 3),
+        "stream_read_K": {"bytes": int(K.numel() * K.element_size()), "kernel_us_median": round(statistics.median(read_us), 3),
                           "GBps": round(read_GBps, 1)},
     }
     if dense_us is not None:

@@ -237,13 +237,16 @@ void santa_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t 
 double santa_exp_f64(double x);
 
 /*
- * santa_stream_read — diagnostic: reads `bytes` of device memory at `src` once with the 16-byte
- * non-temporal loads the score pass uses for K, writing one XOR word per block into `scratch` (device
- * memory of santa_stream_read_scratch_bytes() bytes, contents meaningless). Timed around the call on
- * the caller's stream, it measures the read bandwidth the device reaches for that size and cache state.
- * bytes must be a positive multiple of 16 and src 16-byte aligned; asynchronous like the decode calls.
+ * santa_stream_read — diagnostic: reads `bytes` of device memory at `src` once with 16-byte non-temporal
+ * loads (the loads the score pass streams K with; one block of 1024 threads per CU, 128 KiB in flight per
+ * CU), writing one XOR word per block into `scratch` (device memory of santa_stream_read_scratch_bytes()
+ * bytes, contents meaningless): the read bandwidth the device reaches for that size and cache state.
+ * bytes must be a positive multiple of 16 and src 16-byte aligned; asynchronous like the decode calls,
+ * unless kernel_ms (host, optional) is given: then the call synchronises and stores the kernel's
+ * execution time in milliseconds from events HIP records at the kernel's own start and end.
  */
-int santa_stream_read(const void* src, size_t bytes, void* scratch, size_t scratch_bytes, void* stream);
+int santa_stream_read(const void* src, size_t bytes, void* scratch, size_t scratch_bytes, void* stream,
+                      float* kernel_ms);
 size_t santa_stream_read_scratch_bytes(void);
 
 const char* santa_status_string(int status);

@@ -114,7 +114,7 @@ def lib() -> ctypes.CDLL:
         L.santa_release.argtypes = []
         L.santa_stream_read.restype = ctypes.c_int
         L.santa_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
-                                        ctypes.c_void_p]
+                                        ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]
         L.santa_stream_read_scratch_bytes.restype = ctypes.c_size_t
         L.santa_stream_read_scratch_bytes.argtypes = []
         _lib = L
@@ -346,9 +346,10 @@ def dense_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, *, nk: int |
     return out
 
 
-def stream_read(t: torch.Tensor, scratch: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+def stream_read(t: torch.Tensor, scratch: torch.Tensor | None = None, stream=None, kernel_time: bool = False):
     """Reads the bytes of a contiguous device tensor once through santa_stream_read (a bandwidth probe);
-    returns the scratch tensor holding one XOR word per block."""
+    returns the scratch tensor holding one XOR word per block, or (scratch, kernel milliseconds) with
+    kernel_time (events at the kernel's own start and end; synchronises)."""
     if not t.is_contiguous():
         raise ValueError("stream_read needs a contiguous tensor")
     need = int(lib().santa_stream_read_scratch_bytes())
@@ -357,9 +358,11 @@ def stream_read(t: torch.Tensor, scratch: torch.Tensor | None = None, stream=Non
     if stream is None:
         stream = torch.cuda.current_stream(t.device)
     st = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    ms = ctypes.c_float(0.0)
     _check(lib().santa_stream_read(t.data_ptr(), t.numel() * t.element_size(), scratch.data_ptr(),
-                                   scratch.numel() * scratch.element_size(), st))
-    return scratch
+                                   scratch.numel() * scratch.element_size(), st,
+                                   ctypes.byref(ms) if kernel_time else None))
+    return (scratch, float(ms.value)) if kernel_time else scratch
 
 
 def philox4x32_10(ctr, key):

@@ -84,7 +84,9 @@ __global__ __launch_bounds__(THREADS) void dense_partial_kernel(DenseProblem p) 
   __shared__ float wl[THREADS / 64][NRG][GM];
   __shared__ float wacc[THREADS / 64][NRG][GM][D];
 
-  const int t = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  // the KV heads of a position are adjacent in memory: blocks of one chunk for every KV head run side by
+  // side (grid x = KV head), so the rows they stream share DRAM pages
+  const int kv = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = p.G;
   const int rg = lane / LPR, pc = lane % LPR;
@@ -260,19 +262,20 @@ __global__ __launch_bounds__(THREADS) void dense_partial_kernel(DenseProblem p) 
   }
 }
 
-// merge: block per (head, sequence). Thread (slice sl, element e) folds chunks sl, sl + SL, ... into a
-// running (max, sum-exp, weighted sum) with the loads of MB chunks in flight at once; the SL slices are
-// then combined the same way.
+// merge: block per (head, sequence, MCOLS columns). Thread (slice sl, column e) folds chunks sl, sl + SL,
+// ... into a running (max, sum-exp, weighted sum) with the loads of MB chunks in flight at once; the SL
+// slices are then combined the same way.
 constexpr int MERGE_THREADS = 512;
+constexpr int MCOLS = 32;
 constexpr int MB = 16;
 template <int D, bool BF16>
 __global__ __launch_bounds__(MERGE_THREADS) void dense_merge_kernel(DenseProblem p) {
-  constexpr int SL = MERGE_THREADS / D;
+  constexpr int SL = MERGE_THREADS / MCOLS;
   __shared__ float sm[SL];
   __shared__ float sls[SL];
-  __shared__ float so[SL][D];
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, e = tid % D, sl = tid / D;
+  __shared__ float so[SL][MCOLS];
+  const int h = blockIdx.x, b = blockIdx.y, c0 = blockIdx.z * MCOLS;
+  const int tid = threadIdx.x, e = c0 + tid % MCOLS, sl = tid / MCOLS;
   const int Td = p.Td;
   const float* src = p.part + ((int64_t)b * p.H + h) * Td * (D + 2);
   float M = -INFINITY, L = 0.f, O = 0.f;
@@ -301,13 +304,13 @@ __global__ __launch_bounds__(MERGE_THREADS) void dense_merge_kernel(DenseProblem
     }
     M = mb;
   }
-  so[sl][e] = O;
-  if (e == 0) {
+  so[sl][tid % MCOLS] = O;
+  if (tid % MCOLS == 0) {
     sm[sl] = M;
     sls[sl] = L;
   }
   __syncthreads();
-  if (tid < D) {
+  if (tid < MCOLS) {
     float Mx = sm[0];
     for (int k = 1; k < SL; ++k) Mx = fmaxf(Mx, sm[k]);
     float r = 0.f, l = 0.f;
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(MERGE_THREADS) void dense_merge_kernel(DenseProblem
       l += f * sls[k];
     }
     r /= l;
-    const int64_t oi = ((int64_t)b * p.H + h) * D + tid;
+    const int64_t oi = ((int64_t)b * p.H + h) * D + c0 + tid;
     if (BF16)
       ((uint16_t*)p.out)[oi] = f32_to_bf16_rne(r);
     else
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(MERGE_THREADS) void dense_merge_kernel(DenseProblem
 
 template <int D, bool BF16>
 hipError_t launch_dense_dt(const DenseProblem& p, hipStream_t st) {
-  dim3 grid(p.Td, p.Hkv, p.B);
+  dim3 grid(p.Hkv, p.Td, p.B);
   if (p.G <= 1)
     dense_partial_kernel<D, BF16, 1><<<grid, THREADS, 0, st>>>(p);
   else if (p.G <= 2)
@@ -338,7 +341,7 @@ hipError_t launch_dense_dt(const DenseProblem& p, hipStream_t st) {
     dense_partial_kernel<D, BF16, 8><<<grid, THREADS, 0, st>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dense_merge_kernel<D, BF16><<<dim3(p.H, p.B), MERGE_THREADS, 0, st>>>(p);
+  dense_merge_kernel<D, BF16><<<dim3(p.H, p.B, D / MCOLS), MERGE_THREADS, 0, st>>>(p);
   return hipGetLastError();
 }
 

@@ -57,6 +57,7 @@ hipError_t launch_dense(const DenseProblem& p, hipStream_t st);
 // streaming read probe (util.hip): one XOR word per block into out[blocks]
 constexpr int STREAM_READ_MAX_BLOCKS = 4096;
 int stream_read_blocks(int64_t bytes, int cus);
-hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* out, int blocks, hipStream_t st);
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* out, int blocks, hipStream_t st,
+                              const LaunchEvents& ev = {});
 
 }  // namespace santa

@@ -566,7 +566,8 @@ int santa_dense_decode(const santa_args* a) {
 
 size_t santa_stream_read_scratch_bytes(void) { return (size_t)STREAM_READ_MAX_BLOCKS * sizeof(uint32_t); }
 
-int santa_stream_read(const void* src, size_t bytes, void* scratch, size_t scratch_bytes, void* stream) {
+int santa_stream_read(const void* src, size_t bytes, void* scratch, size_t scratch_bytes, void* stream,
+                      float* kernel_ms) {
   g_err.clear();
   if (!src || !scratch) return fail(SANTA_ERR_INVALID_ARG, "src and scratch must be non-NULL");
   if (bytes < 16 || bytes % 16 || (uintptr_t)src % 16)
@@ -576,8 +577,20 @@ int santa_stream_read(const void* src, size_t bytes, void* scratch, size_t scrat
                 santa_stream_read_scratch_bytes());
   (void)hipGetLastError();
   const int blocks = stream_read_blocks((int64_t)bytes, device_cus());
-  const hipError_t e = launch_stream_read(src, (int64_t)bytes, (uint32_t*)scratch, blocks, (hipStream_t)stream);
+  Events ev;
+  LaunchEvents lev;
+  hipError_t e;
+  if (kernel_ms) {
+    for (int i = 0; i < 2; ++i)
+      if ((e = hipEventCreate(&ev.e[i])) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    lev = LaunchEvents{ev.e[0], ev.e[1]};
+  }
+  e = launch_stream_read(src, (int64_t)bytes, (uint32_t*)scratch, blocks, (hipStream_t)stream, lev);
   if (e != hipSuccess) return hip_fail(e, "stream read kernel launch");
+  if (kernel_ms) {
+    if ((e = hipEventSynchronize(ev.e[1])) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    if ((e = hipEventElapsedTime(kernel_ms, ev.e[0], ev.e[1])) != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+  }
   return SANTA_OK;
 }
 

@@ -10,10 +10,10 @@ namespace santa {
 
 namespace {
 
-constexpr int RT = 256;
-constexpr int UNR = 8;  // loads in flight per thread
+constexpr int RT = 1024;  // one block of 16 waves per CU
+constexpr int UNR = 8;    // loads in flight per thread: 128 KiB per CU
 
-__global__ __launch_bounds__(RT) void stream_read_kernel(const uint4* src, int64_t n16, uint32_t* out) {
+__global__ __launch_bounds__(RT, 1) void stream_read_kernel(const uint4* src, int64_t n16, uint32_t* out) {
   __shared__ uint32_t red[RT / 64];
   const int64_t stride = (int64_t)gridDim.x * RT;
   int64_t i = (int64_t)blockIdx.x * RT + threadIdx.x;
@@ -50,9 +50,9 @@ int stream_read_blocks(int64_t bytes, int cus) {
   return (int)(b < 1 ? 1 : b);
 }
 
-hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* out, int blocks, hipStream_t st) {
-  stream_read_kernel<<<blocks, RT, 0, st>>>((const uint4*)src, bytes / 16, out);
-  return hipGetLastError();
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* out, int blocks, hipStream_t st,
+                              const LaunchEvents& ev) {
+  return launch_timed(stream_read_kernel, dim3(blocks), dim3(RT), st, ev, (const uint4*)src, bytes / 16, out);
 }
 
 }  // namespace santa

@@ -111,12 +111,12 @@ def test_stream_read_validation(L):
     """The bandwidth probe validates its arguments before any HIP call."""
     need = L.santa_stream_read_scratch_bytes()
     assert need >= 4 * 1024
-    assert L.santa_stream_read(None, 1024, 4096, need, None) == santa.ERR_INVALID_ARG
-    assert L.santa_stream_read(4096, 1024, None, need, None) == santa.ERR_INVALID_ARG
-    assert L.santa_stream_read(4096, 1000, 8192, need, None) == santa.ERR_INVALID_ARG  # not a multiple of 16
-    assert L.santa_stream_read(4104, 1024, 8192, need, None) == santa.ERR_INVALID_ARG  # src not 16-byte aligned
-    assert L.santa_stream_read(4096, 0, 8192, need, None) == santa.ERR_INVALID_ARG
-    assert L.santa_stream_read(4096, 1024, 8192, need - 4, None) == santa.ERR_WORKSPACE
+    assert L.santa_stream_read(None, 1024, 4096, need, None, None) == santa.ERR_INVALID_ARG
+    assert L.santa_stream_read(4096, 1024, None, need, None, None) == santa.ERR_INVALID_ARG
+    assert L.santa_stream_read(4096, 1000, 8192, need, None, None) == santa.ERR_INVALID_ARG  # not a multiple of 16
+    assert L.santa_stream_read(4104, 1024, 8192, need, None, None) == santa.ERR_INVALID_ARG  # src not 16-byte aligned
+    assert L.santa_stream_read(4096, 0, 8192, need, None, None) == santa.ERR_INVALID_ARG
+    assert L.santa_stream_read(4096, 1024, 8192, need - 4, None, None) == santa.ERR_WORKSPACE
 
 
 def test_workspace_bytes(L):
