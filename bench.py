@@ -4,16 +4,19 @@ Workload (default): Llama-3.1-8B-shaped single-layer decode, batch 1, 32 query /
 bf16 K/V cache of nk=32768 positions with 32 planted aligned keys per query head, stratified sampling
 with S=256 (seeded synthetic inputs, resident in HBM before timing).
 
-A step is one call of santa_decode_ex (score -> chunk CDF -> resolve+gather per chunk -> merge), timed with HIP events on the
-launching stream. Before every timed step a 1 GiB in-place update evicts K/V from the caches (the
-256 MB Infinity Cache would otherwise hold the 64 MiB K), outside the events, like the cold-cache
-protocol of the paper's kernel benchmark (Appendix Q). Reported alongside:
+A step is one call of santa_decode_ex, timed with HIP events on the launching stream. On this workload
+the call is one kernel launch (score phase, group barrier, chunk CDF, sampling, gather, output sum);
+other shapes run score -> sampling+gather per chunk -> merge. Before every timed step a 1 GiB in-place
+update evicts K/V from the caches (the 256 MB Infinity Cache would otherwise hold the 64 MiB K), outside
+the events, like the cold-cache protocol of the paper's kernel benchmark (Appendix Q). Reported alongside:
   * the dense bf16 decode baseline of the same library on the same inputs and protocol;
-  * per-stage times (a separate pass, same protocol): the score kernel's execution time from HIP events
-    recorded at the kernel's own start and end on the launching stream, which gives the roofline of the
-    dominant kernel (the score pass: algorithmic bytes = K + q per launch), and the later stages from
-    events between the launches;
+  * the roofline of the dominant kernel (the one-launch decode kernel where it runs, else the score
+    kernel): its algorithmic bytes over its execution time, from HIP events recorded at the kernel's own
+    start and end (a separate pass, same protocol); its measured HBM bytes from the committed rocprofv3
+    counter record while the kernel sources are unchanged; the device's read rate on the same K bytes from
+    a streaming-read probe timed the same way;
   * the same step captured into a HIP graph and replayed (same protocol);
+  * S2ANTA-prop, S2ANTA-flash, feature-major K^T variants and one GPU's share of an 8-way head split;
   * the fp64 oracle timed on the host's cores on the same inputs (a baseline, not the target).
 
 Prints one JSON line. --gpus N > 1 is refused: the benchmark runs on one GPU.
