@@ -412,12 +412,11 @@ struct Problem {
   int spin_limit;        // polls before a bounded wait gives up (the block then flags itself)
   int32_t* status;       // [B, Hkv] per call: 0, or 1 if a bounded wait of the group's blocks gave up
   bool check_sync;       // the merge reads the streaming score blocks' handshake flags (sync_err)
-  // one-launch decode (KM_DECODE): epoch per group, arrival flags and error word per block (grid index
-  // (b * Hkv + kv) * P + r); the per-block partial output sums live in `partial` as [blocks, G, d]
+  // one-launch decode (KM_DECODE): epoch per group and started flag per block (grid index
+  // (b * Hkv + kv) * P + r); the chunk statistics are cmax / csum, the per-block partial output sums
+  // live in `partial` as [blocks, G, d]
   uint64_t* sync_epoch;  // [SYNC_MAX_GROUPS]
-  uint64_t* sync_flag_a; // [SYNC_MAX_BLOCKS] chunk statistics published
-  uint64_t* sync_flag_b; // [SYNC_MAX_BLOCKS] partial sums published
-  uint32_t* sync_block_err;  // [SYNC_MAX_BLOCKS]
+  uint64_t* sync_start;  // [SYNC_MAX_BLOCKS] started flags: the block's published words are VOID
   bool one_launch;       // the whole decode runs in the score kernel
 };
 

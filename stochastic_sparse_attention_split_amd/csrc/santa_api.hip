@@ -42,10 +42,9 @@ struct Layout {
       kfeat, bmap, total;
 };
 
-// the synchronisation region of the one-launch decode, at offset 0 of every workspace: epochs per group,
-// arrival flags and error words per block
-constexpr size_t SYNC_BYTES =
-    SYNC_MAX_GROUPS * sizeof(uint64_t) + 2 * SYNC_MAX_BLOCKS * sizeof(uint64_t) + SYNC_MAX_BLOCKS * sizeof(uint32_t);
+// the synchronisation region of the one-launch decode, at offset 0 of every workspace: epochs per group
+// and started flags per block
+constexpr size_t SYNC_BYTES = SYNC_MAX_GROUPS * sizeof(uint64_t) + SYNC_MAX_BLOCKS * sizeof(uint64_t);
 
 // every region is written by the call before it is read: no initial contents are required
 // sampled keys listed per head: S, or T * S_tile for S²ANTA-flash
@@ -294,9 +293,7 @@ int santa_decode_ex(const santa_args* a) {
   p.status = (int32_t*)(ws + L.status);
   p.check_sync = p.bf16 && !p.kfm;  // the streaming score kernel flags its blocks' handshakes
   p.sync_epoch = (uint64_t*)(ws + L.sync);
-  p.sync_flag_a = p.sync_epoch + SYNC_MAX_GROUPS;
-  p.sync_flag_b = p.sync_flag_a + SYNC_MAX_BLOCKS;
-  p.sync_block_err = (uint32_t*)(p.sync_flag_b + SYNC_MAX_BLOCKS);
+  p.sync_start = p.sync_epoch + SYNC_MAX_GROUPS;
   const int one = (a->mode & SANTA_MULTI_LAUNCH) ? 0 : one_launch_blocks(p, device_cus());
   p.one_launch = one > 0;
   if (p.one_launch) p.score_blocks_per_group = one;

@@ -85,32 +85,6 @@ __device__ inline int tile_off(int row, int pc) {
   return row * SGeo<D>::ROWB + ((pc ^ (row % SGeo<D>::PPR)) << 4);
 }
 
-// One-launch decode: the chunk CDF of one head (Appendix O, Algorithm 4) from the chunk statistics its
-// group's blocks published (coherent device-scope loads), lane l owning chunks [l PER, (l + 1) PER); the
-// edges C_0..C_T and the chunk scales exp(m_t - m*) go to LDS (cg, sg). Returns (Z, last chunk with mass).
-template <int PER>
-__device__ inline double2 cdf_to_lds(const double* cm, const double* cs, int T, int lane, double* cg, double* sg) {
-  double m[PER], l[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {  // lanes past T re-read the last chunk (masked)
-    const int tt = min(lane * PER + j, T - 1);
-    m[j] = __hip_atomic_load(cm + tt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    l[j] = __hip_atomic_load(cs + tt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  ChunkCdf<PER> o;
-  chunk_cdf_wave<PER>(m, l, T, lane, o);
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int t = lane * PER + j;
-    if (t < T) {
-      cg[t] = o.c[j];
-      sg[t] = o.f[j];
-    }
-  }
-  if (lane == 0) cg[T] = o.top;  // the last chunk ends at the total
-  return make_double2(o.top, (double)o.last);
-}
-
 // Bounded poll of n flags in device memory (one wave; flags are read with coherent device-scope loads):
 // true once every flag equals `target`, false after `limit` checks. Up to 64 flags, four rounds of loads
 // stay in flight, spaced in time, each checked as it returns, so a flag is seen about a quarter of a
@@ -147,6 +121,73 @@ __device__ inline bool poll_flags(const uint64_t* flags, int n, uint64_t target,
     if (spins >= limit) return false;
     __builtin_amdgcn_s_sleep(1);
   }
+}
+
+// One-launch decode: the words that blocks of a group exchange (chunk statistics, partial sums) hold
+// VOID until this call writes them, or FAIL when their block gave up. Both are signalling NaNs with
+// low payload bits set, which no computation here yields: arithmetic returns quiet NaNs, and NaNs
+// carried over from bf16 inputs have all low payload bits clear. Words are compared as bit patterns.
+constexpr uint64_t D_VOID = 0xFFF4C0DE00000001ull, D_FAIL = 0xFFF4C0DE00000002ull;
+constexpr uint32_t F_VOID = 0xFFA00001u, F_FAIL = 0xFFA00002u;
+
+__device__ inline uint64_t ld_word(const double* f) {
+  return __hip_atomic_load((const uint64_t*)f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_word(double* f, uint64_t v) {
+  __hip_atomic_store((uint64_t*)f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One-launch decode: the chunk CDF of one head (Appendix O, Algorithm 4) from the chunk statistics the
+// blocks of its group publish: loads every word once, then reloads (bounded) the words still VOID; lane
+// l owns chunks [l PER, (l + 1) PER). The
+// edges C_0..C_T and the chunk scales exp(m_t - m*) go to LDS (cg, sg) and (Z, last chunk with mass) to
+// zl. Returns 0, or 1 if a block reported FAIL or the wait gave up.
+template <int PER>
+__device__ inline int cdf_poll_to_lds(const double* cm, const double* cs, int T, int lane, int limit,
+                                      double* cg, double* sg, double2* zl) {
+  uint64_t wm[PER], wl[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {  // lanes past T re-read the last chunk
+    const int tt = min(lane * PER + j, T - 1);
+    wm[j] = ld_word(cm + tt);
+    wl[j] = ld_word(cs + tt);
+  }
+  for (int spins = 0;; ++spins) {
+    bool vd = false;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) vd = vd || wm[j] == D_VOID || wl[j] == D_VOID;
+    if (__ballot(vd) == 0ull) break;
+    if (spins >= limit) return 1;
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {  // only the words still VOID are read again
+      const int tt = min(lane * PER + j, T - 1);
+      if (wm[j] == D_VOID) wm[j] = ld_word(cm + tt);
+      if (wl[j] == D_VOID) wl[j] = ld_word(cs + tt);
+    }
+  }
+  bool fl = false;
+  double m[PER], l[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    fl = fl || wm[j] == D_FAIL || wl[j] == D_FAIL;
+    m[j] = __longlong_as_double((long long)wm[j]);
+    l[j] = __longlong_as_double((long long)wl[j]);
+  }
+  if (__ballot(fl) != 0ull) return 1;
+  ChunkCdf<PER> o;
+  chunk_cdf_wave<PER>(m, l, T, lane, o);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int t = lane * PER + j;
+    if (t < T) {
+      cg[t] = o.c[j];
+      sg[t] = o.f[j];
+    }
+  }
+  if (lane == 0) cg[T] = o.top;  // the last chunk ends at the total
+  *zl = make_double2(o.top, (double)o.last);
+  return 0;
 }
 
 // LDS handshake counters. signal(): this wave's earlier LDS writes (and, for copy waves, the copies
@@ -236,7 +277,7 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   __shared__ double hnorm[HM];
   __shared__ __align__(16) unsigned char qs[1024 * HG];
   __shared__ int rl[FL ? 4 : 1][FL ? CHUNK : 1];  // fused S²ANTA-flash: sampled rows (key | count << 8) per head
-  constexpr int NCTR = 14;
+  constexpr int NCTR = 16;
   __shared__ int ctr[NCTR];
   int* ld = &ctr[0];   // [NBUF]
   int* use = &ctr[4];  // [NBUF]
@@ -246,9 +287,11 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   int* pb = &ctr[11];
   int* fin = &ctr[12];
   int* bad = &ctr[13];
-  __shared__ int dstat[2];      // one-launch decode: barrier outcomes (0 = passed)
+  int* ivd = &ctr[14];  // one-launch decode: copy waves whose VOID stores are complete
+  int* stc = &ctr[15];  // one-launch decode: the started flags of the group have been polled
+  __shared__ int dstat[3];      // one-launch decode: statistics failed, output poisoned, started flags seen
+  __shared__ uint64_t depoch;   // one-launch decode: the group's epoch at the start of this call
   __shared__ int wcnt[STHREADS / 64];
-  uint64_t epoch = 0;           // one-launch decode: the group's epoch, read by the polling wave at its start
   double pv[NRX][4];            // one-launch decode, NREG > 0: this exponential wave's prefix rows
 
   const int kv = blockIdx.y, b = blockIdx.z;
@@ -263,7 +306,8 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   int* err = p.sync_err + ((int64_t)b * gridDim.y + kv) * gridDim.x + t0;
 
   if (tid < NCTR) ctr[tid] = 0;
-  __syncthreads();  // the only block-wide barrier
+  if (tid < 3) dstat[tid] = 0;
+  __syncthreads();  // the only block-wide barrier of the score phase
 
   const int64_t seq_bytes = 2 * p.seq_stride;
   const char* kbase = (const char*)p.K + 2 * ((int64_t)b * p.batch_stride + (int64_t)kv * D);
@@ -286,11 +330,6 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
     // landed. Highest issue priority on their SIMD: they issue rarely and the whole block waits on them.
     __builtin_amdgcn_s_setprio(3);
     const int j = wave - NMF - SSOFT, hh = j & 1;
-    // every block reads its group's epoch before it can publish anything; it changes only after every
-    // block of the group has published its partial sums (see decode_tail)
-    if constexpr (DEC)
-      if (wave == NMF + SSOFT)
-        epoch = __hip_atomic_load(p.sync_epoch + b * p.Hkv + kv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (j == SCOPY - 1) {
       const char* qsrc = (const char*)p.q + ((int64_t)b * p.H + h0) * D * 2;
 #pragma unroll
@@ -299,6 +338,50 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
       wait_vm<0>();
       signal(qr, lane);
     }
+    // One-launch decode: right after its first copies every copy wave sets its share of the words this
+    // block will publish (chunk statistics, partial sums) to VOID; the wait for those copies completes
+    // the stores too. Once all four waves have, the block announces that it has started. A block reads
+    // another block's words only after it has seen that block's started flag, so it sees VOID or this
+    // call's value, never a value left by an earlier call. Block 0 clears the group's status word the
+    // same way.
+    const int grp = b * p.Hkv + kv, me = grp * step + t0;
+    if constexpr (DEC) {
+      // the group's epoch (it changes only after every block of the group has published its partial
+      // sums), read by the last copy wave, whose first copies wait for another wave's anyway, and put in
+      // LDS at once: no load of it is left in flight where the roles join the sampling phase
+      if (j == SCOPY - 1) {
+        const uint64_t e = __hip_atomic_load(p.sync_epoch + grp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) depoch = e;
+      }
+    }
+    bool voided = !DEC, announced = !DEC;
+    auto set_void = [&]() {
+      // statistics words of chunk k: set by the copy wave of its first half, so the wait that precedes
+      // the chunk's scores (and so its genuine statistics) completes them
+      if (hh == 0) {
+        const int nk = n > (j >> 1) ? (n - (j >> 1) + 1) / 2 : 0;  // chunks k = (j >> 1) + 2 m < n
+        for (int i = lane; i < nk * 2 * G; i += 64) {
+          const int k = (j >> 1) + 2 * (i / (2 * G)), g = (i >> 1) % G;
+          st_word(((i & 1) ? p.csum : p.cmax) + ((int64_t)b * p.H + h0 + g) * T + t0 + k * step, D_VOID);
+        }
+      }
+      uint32_t* gpart = reinterpret_cast<uint32_t*>(p.partial) + (int64_t)me * G * D;
+      for (int i = j * 64 + lane; i < G * D; i += SCOPY * 64)
+        __hip_atomic_store(gpart + i, F_VOID, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (j == 0 && t0 == 0 && lane == 0)
+        __hip_atomic_store(p.status + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      voided = true;
+    };
+    auto announce = [&]() {  // this wave's VOID stores are complete
+      if (lane == 0) {
+        // the last copy wave wrote depoch before its own increment of ivd
+        const int before = __hip_atomic_fetch_add(ivd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (before == SCOPY - 1)
+          __hip_atomic_store(p.sync_start + me, ((depoch + 1) << 10) | (uint64_t)grp, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+      announced = true;
+    };
     for (int k = j >> 1, m = 0; k < n && ok; k += 2, ++m) {
       if (m > 0) ok = wait_ge(&use[j], SPH * m, p.spin_limit);  // the buffer's previous half is no longer read
       // the block's second chunk is requested once the same half of its first has landed, so across the
@@ -315,10 +398,23 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
         const int64_t key = h0k + row < p.nk ? h0k + row : c0;  // keys past the end re-read the chunk's first
         copy_to_lds16(kbase + key * seq_bytes + pc * 16, base + i * 1024);
       }
+      if (!voided) set_void();
       wait_vm<0>();
       signal(&ld[j], lane);
+      if (!announced) announce();
     }
+    if (!voided) set_void();
     wait_vm<0>();  // no copy may land after the block ends
+    if constexpr (DEC) {
+      if (!announced) announce();
+      if (j == SCOPY - 1) {  // the started flags of the group, seen before the sampling phase needs them
+        const uint64_t target = ((depoch + 1) << 10) | (uint64_t)grp;
+        bool seen = wait_ge(ivd, SCOPY, p.spin_limit);
+        seen = seen && poll_flags(p.sync_start + (int64_t)grp * step, step, target, lane, p.spin_limit);
+        if (lane == 0) dstat[2] = seen ? 1 : 2;
+        signal(stc, lane);
+      }
+    }
     SK_PHASE1_DONE();
   }
 
@@ -680,19 +776,22 @@ decode_tail: __attribute__((unused));
     // ==== one-launch decode: sampling and gather after the score phase ====
     // ("Stochastic Sparse Attention for Memory-Bound Inference", Section 3.1: the global barrier between
     // the split-K statistics and the sampling; Appendix O, Algorithms 4 and 5.) The blocks of a (KV head,
-    // sequence) group share nothing but device memory: each publishes its chunk statistics, waits until
-    // every block of the group has (barrier A), builds the chunk CDF of each head, resolves the points
-    // that fall in its own chunks from its own prefix rows, gathers each sampled V row once for the group
-    // and publishes its per-head partial sums; block 0 of the group waits for every block's partials,
-    // adds them in block order (fp64) and scales by 1/S.
+    // sequence) group share nothing but device memory: each publishes its chunk statistics, builds the
+    // chunk CDF of each head from every block's statistics, resolves the points that fall in its own
+    // chunks from its own prefix rows, gathers each sampled V row once for the group and publishes its
+    // per-head partial sums; each block then adds the group's partials of a slice of the outputs in
+    // block order (fp64) and scales by 1/S.
     // Cross-block data travel only as device-scope relaxed atomic stores and loads, which this chip keeps
-    // coherent across its L2s without a cache write-back; a flag is stored only after the data it
-    // announces have completed (vmcnt(0)). Flags carry ((epoch + 1) << 10 | group): the epoch of a group
-    // is read by every block at its start and advanced once every block of the group has published its
+    // coherent across its L2s without a cache write-back. The published words are VOID until written
+    // (see the start of the exponential waves), so a reader waits for the data themselves instead of for
+    // a flag stored after them. Started flags carry ((epoch + 1) << 10 | group): the epoch of a group is
+    // read by every block at its start and advanced once every block of the group has published its
     // partial sums, so flags left by earlier calls never match and the workspace needs no initial contents.
     __builtin_amdgcn_s_setprio(0);
     if (!ok && lane == 0) __hip_atomic_fetch_or(bad, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    wait_vm<0>();  // this wave's statistics, prefix-row and probability stores are complete
+    // prefix rows (NREG = 0) and debug probabilities stored above are read back below, partly by other
+    // waves: this wave's stores must be complete first
+    if (NREG == 0 || p.prob != nullptr) wait_vm<0>();
     __syncthreads();
     constexpr int GM = 4 * HG;      // head slots of the counters
     constexpr int NCW = GM / 2;     // 32-bit words of 16-bit per-head counts per key
@@ -700,8 +799,7 @@ decode_tail: __attribute__((unused));
     const int P = step, r = t0;
     const int grp = b * p.Hkv + kv;
     const int me = grp * P + r;
-    const bool poller = wave == NMF + SSOFT;
-    const uint64_t target = ((epoch + 1) << 10) | (uint64_t)grp;  // meaningful in the polling wave only
+    const bool failed = *bad != 0;  // block-uniform: a wait of the score phase gave up
     // the K tiles are free now (layout: decode_lds_plan, checked on the host)
     const DecodeLds LP = decode_lds_plan(G, n, T, sizeof(kt));
     unsigned char* lds = &kt[0][0];
@@ -744,33 +842,38 @@ decode_tail: __attribute__((unused));
           for (int i = 0; i < 4; ++i) rowg[kk * CHUNK + 4 * lane + i] = v[kk][i];
     };
 
-    // -- barrier A: every block of the group has published its chunk statistics. Meanwhile the head
-    // waves put their first prefix rows into LDS, which needs no statistics.
-    if (poller) {
-      if (lane == 0) __hip_atomic_store(p.sync_flag_a + me, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool passed = poll_flags(p.sync_flag_a + (int64_t)grp * P, P, target, lane, p.spin_limit);
-      if (lane == 0) dstat[0] = passed ? 0 : 1;
-    }
+    // a block whose score phase gave up publishes FAIL for its chunks, so no reader waits for them
+    if (failed && headwave && lane < 2 * n)
+      st_word(((lane & 1) ? p.csum : p.cmax) + bhw * T + t0 + (lane >> 1) * P, D_FAIL);
     const double u_sys =
         headwave && p.mode == 2 ? uniform53(p.seed, 0u, (uint32_t)(h0 + hw), (uint32_t)b, TAG_SYS) : 0.0;
     if (headwave) put_rows(0);
-    __syncthreads();
-    const bool good = dstat[0] == 0 && *bad == 0;  // block-uniform
+    __syncthreads();  // the counters and the bitmap are clear
 
-    // -- points of each head that fall in this block's chunks (one wave per head)
-    if (good && headwave) {
+    // -- each head's chunk CDF from the group's statistics, then the points of the head that fall in this
+    // block's chunks (one wave per head)
+    int hst = 1;  // wave-uniform: 0 once this head wave's chunk CDF is in LDS
+    double2 zl = make_double2(0.0, 0.0);
+    if (!failed && headwave) {
+      double* cg = cdfl + (size_t)hw * (T + 1);
+      double* sg = scl + (size_t)hw * T;
+      // every block's started flag has been seen (exponential wave 0 of this block)
+      if (wait_ge(stc, 1, p.spin_limit) && dstat[2] == 1) {
+        // lane l owns chunks [l PER, (l + 1) PER) with PER the power of two the multi-launch path uses
+        // for this T (the same edges, bit for bit)
+        const double* cmg = p.cmax + bhw * T;
+        const double* csg = p.csum + bhw * T;
+        if (T <= 64) hst = cdf_poll_to_lds<1>(cmg, csg, T, lane, p.spin_limit, cg, sg, &zl);
+        else if (T <= 128) hst = cdf_poll_to_lds<2>(cmg, csg, T, lane, p.spin_limit, cg, sg, &zl);
+        else if (T <= 256) hst = cdf_poll_to_lds<4>(cmg, csg, T, lane, p.spin_limit, cg, sg, &zl);
+        else hst = cdf_poll_to_lds<8>(cmg, csg, T, lane, p.spin_limit, cg, sg, &zl);
+      }
+      if (hst != 0 && lane == 0) __hip_atomic_fetch_or(&dstat[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    if (hst == 0) {
       const int g = hw, h = h0 + hw;
       double* cg = cdfl + (size_t)g * (T + 1);
       double* sg = scl + (size_t)g * T;
-      // the head's chunk CDF, lane l owning chunks [l PER, (l + 1) PER) with PER the power of two the
-      // multi-launch path uses for this T (the same edges, bit for bit), written to LDS
-      const double* cmg = p.cmax + bhw * T;
-      const double* csg = p.csum + bhw * T;
-      double2 zl;
-      if (T <= 64) zl = cdf_to_lds<1>(cmg, csg, T, lane, cg, sg);
-      else if (T <= 128) zl = cdf_to_lds<2>(cmg, csg, T, lane, cg, sg);
-      else if (T <= 256) zl = cdf_to_lds<4>(cmg, csg, T, lane, cg, sg);
-      else zl = cdf_to_lds<8>(cmg, csg, T, lane, cg, sg);
       const double Z = zl.x;
       const int lastc = (int)zl.y;
       // (the products with 1/Z may round differently from the quotients; the +-1 margin of the candidate
@@ -852,6 +955,7 @@ decode_tail: __attribute__((unused));
       }
     }
     __syncthreads();
+    const bool good = !failed && dstat[0] == 0;  // block-uniform
 
     // -- compaction (one wave): the block's sampled keys in slot order, distinct keys per chunk
     if (wave == 0) {
@@ -950,57 +1054,57 @@ decode_tail: __attribute__((unused));
     }
     __syncthreads();
     const int GD = G * D;
-    float* gpart = p.partial + (int64_t)me * GD;
+    uint32_t* gpart = reinterpret_cast<uint32_t*>(p.partial) + (int64_t)me * GD;
     for (int i = tid; i < GD; i += STHREADS) {
       const int g = i / D, e = i % D;
       float sum = 0.0f;
 #pragma unroll
       for (int w = 0; w < NRGS; ++w) sum += wsum[((size_t)w * GM + g) * D + e];
-      __hip_atomic_store(gpart + i, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gpart + i, good ? __float_as_uint(sum) : F_FAIL, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (tid == 0) __hip_atomic_store(p.sync_block_err + me, good ? 0u : 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    wait_vm<0>();
-    __syncthreads();
+    __syncthreads();  // wsum has been read: its LDS is reused below
 
-    // -- publish; block 0 of the group waits until every block's partials are published, then sums them
-    if (poller) {
-      if (lane == 0) __hip_atomic_store(p.sync_flag_b + me, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (r == 0) {
-        const bool passed = poll_flags(p.sync_flag_b + (int64_t)grp * P, P, target, lane, p.spin_limit);
-        bool e = false;
-        for (int i = lane; i < P; i += 64)
-          e = (__hip_atomic_load(p.sync_block_err + (int64_t)grp * P + i, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT) != 0u) || e;
-        const bool anyerr = !passed || __ballot(e) != 0ull;
-        if (lane == 0) {
-          dstat[1] = anyerr ? 3 : 1;
-          // every block of the group has started (or the wait gave up): the epoch may advance
-          __hip_atomic_store(p.status + grp, anyerr ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(p.sync_epoch + grp, epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      } else if (lane == 0) {
-        dstat[1] = 0;
+    // -- outputs: block r adds the group's P partials of outputs [r per, (r + 1) per) (fp64, in a fixed
+    // order), times 1/S, waiting (bounded) for each partial word while it is VOID. A FAIL word, or a wait
+    // that gave up, makes the block's outputs NaN and sets the group's status word: by block 0, which
+    // cleared it, or by a block that has seen block 0's started flag, stored after that clear.
+    const int per = (GD + P - 1) / P;
+    const int o0 = r * per, no = max(0, min(GD - o0, per));
+    float* fin = reinterpret_cast<float*>(lds);  // [P][no]
+    const uint32_t* gparts = reinterpret_cast<const uint32_t*>(p.partial) + (int64_t)grp * P * GD + o0;
+    bool fbad = false;
+    for (int j = tid; j < no * P; j += STHREADS) {
+      const int i = j / no, e = j - i * no;
+      const uint32_t* src = gparts + (int64_t)i * GD + e;
+      uint32_t v = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int spins = 0; v == F_VOID && spins < p.spin_limit; ++spins) {
+        __builtin_amdgcn_s_sleep(2);
+        v = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      fbad = fbad || v == F_VOID || v == F_FAIL;
+      fin[j] = __uint_as_float(v);
     }
+    if (fbad) __hip_atomic_fetch_or(&dstat[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     __syncthreads();
-    if (dstat[1] & 1) {  // block-uniform: the G x D outputs, the P partials added in block order, times 1/S
-      const bool poisoned = (dstat[1] & 2) != 0;
-      for (int o2 = tid; o2 < GD; o2 += STHREADS) {
-        double sum = 0.0;
-        for (int i0 = 0; i0 < P; i0 += 32) {
-          float v[32];
+    const bool poisoned = dstat[1] != 0;  // block-uniform
+    for (int e0 = tid >> 4; e0 < no; e0 += STHREADS / 16) {  // 16 threads per output, a fixed tree
+      const int q = tid & 15;
+      double sum = 0.0;
+      for (int i = q; i < P; i += 16) sum += (double)fin[i * no + e0];
 #pragma unroll
-          for (int q = 0; q < 32; ++q)  // clamped: every load is valid
-            v[q] = __hip_atomic_load(p.partial + (int64_t)(grp * P + min(i0 + q, P - 1)) * GD + o2, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-          for (int q = 0; q < 32; ++q)
-            if (i0 + q < P) sum += (double)v[q];
-        }
-        const int g = o2 / D, e = o2 % D;
+      for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
+      if (q == 0) {
+        const int o2 = o0 + e0, g = o2 / D, e = o2 % D;
         const int64_t dst = ((int64_t)b * p.H + h0 + g) * D + e;
         ((uint16_t*)p.out)[dst] = poisoned ? (uint16_t)0x7FC0u : f64_to_bf16_rne(sum / (double)p.S);
       }
+    }
+    if (tid == 0) {
+      if (poisoned && (r == 0 || dstat[2] == 1))
+        __hip_atomic_fetch_or(p.status + grp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // block 0 has seen every block's partial words (its slice reads all P blocks), so every block of
+      // the group has read the epoch: it may advance
+      if (r == 0) __hip_atomic_store(p.sync_epoch + grp, depoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
