@@ -418,6 +418,7 @@ struct Problem {
   uint64_t* sync_epoch;  // [SYNC_MAX_GROUPS]
   uint64_t* sync_start;  // [SYNC_MAX_BLOCKS] started flags: the block's published words are VOID
   bool one_launch;       // the whole decode runs in the score kernel
+  int lds_nb, lds_cnt, lds_list, lds_bits, lds_cdf, lds_scl, lds_rows;  // its sampling phase's LDS plan
 };
 
 // LDS plan of the sampling phase of the one-launch decode for G heads, n chunks per block and T chunks

@@ -296,7 +296,18 @@ int santa_decode_ex(const santa_args* a) {
   p.sync_start = p.sync_epoch + SYNC_MAX_GROUPS;
   const int one = (a->mode & SANTA_MULTI_LAUNCH) ? 0 : one_launch_blocks(p, device_cus());
   p.one_launch = one > 0;
-  if (p.one_launch) p.score_blocks_per_group = one;
+  if (p.one_launch) {
+    p.score_blocks_per_group = one;
+    // the sampling phase's LDS plan for the largest chunk count of a block (checked to fit above)
+    const DecodeLds L = decode_lds_plan(p.G, (p.T + one - 1) / one, p.T, decode_lds_capacity(p.d));
+    p.lds_nb = L.nb;
+    p.lds_cnt = (int)L.cnt;
+    p.lds_list = (int)L.list;
+    p.lds_bits = (int)L.bits;
+    p.lds_cdf = (int)L.cdf;
+    p.lds_scl = (int)L.scl;
+    p.lds_rows = (int)L.rows;
+  }
 
   hipStream_t stream = (hipStream_t)a->stream;
   Events ev;

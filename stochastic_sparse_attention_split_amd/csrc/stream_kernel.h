@@ -789,31 +789,40 @@ decode_tail: __attribute__((unused));
     // partial sums, so flags left by earlier calls never match and the workspace needs no initial contents.
     __builtin_amdgcn_s_setprio(0);
     if (!ok && lane == 0) __hip_atomic_fetch_or(bad, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // The matrix waves are done (their last LDS reads are behind them): they end here, and the sampling
+    // phase runs on the exponential and copy waves. A wave that has ended is not waited for at a barrier.
+    if (wave < NMF) return;
+    constexpr int NW = SSOFT + SCOPY;  // waves of the sampling phase
+    constexpr int TT = 64 * NW;        // its threads
+    const int tw = wave - NMF, ttid = tid - 64 * NMF;
     // prefix rows (NREG = 0) and debug probabilities stored above are read back below, partly by other
     // waves: this wave's stores must be complete first
     if (NREG == 0 || p.prob != nullptr) wait_vm<0>();
     __syncthreads();
     constexpr int GM = 4 * HG;      // head slots of the counters
     constexpr int NCW = GM / 2;     // 32-bit words of 16-bit per-head counts per key
-    constexpr int NW = STHREADS / 64;
     const int P = step, r = t0;
     const int grp = b * p.Hkv + kv;
     const int me = grp * P + r;
     const bool failed = *bad != 0;  // block-uniform: a wait of the score phase gave up
-    // the K tiles are free now (layout: decode_lds_plan, checked on the host)
-    const DecodeLds LP = decode_lds_plan(G, n, T, sizeof(kt));
+    // the K tiles are free now (layout: decode_lds_plan for the group's largest chunk count, computed on
+    // the host)
+    struct {
+      int nb;
+    } LP = {p.lds_nb};
     unsigned char* lds = &kt[0][0];
-    uint32_t* cnt = reinterpret_cast<uint32_t*>(lds + LP.cnt);    // [n][CHUNK][NCW]
-    int32_t* list = reinterpret_cast<int32_t*>(lds + LP.list);    // sampled keys, slot k * CHUNK + j
-    uint32_t* bits = reinterpret_cast<uint32_t*>(lds + LP.bits);  // [n * CHUNK / 32] sampled-key bitmap
-    double* cdfl = reinterpret_cast<double*>(lds + LP.cdf);       // [G][T + 1] chunk CDF C_t of each head
-    double* scl = reinterpret_cast<double*>(lds + LP.scl);        // [G][T] chunk scales exp(m_t - m*)
-    double* rows = reinterpret_cast<double*>(lds + LP.rows);      // [G][nb][CHUNK] prefix rows
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(lds + p.lds_cnt);    // [n][CHUNK][NCW]
+    int32_t* list = reinterpret_cast<int32_t*>(lds + p.lds_list);    // sampled keys, slot k * CHUNK + j
+    uint32_t* bits = reinterpret_cast<uint32_t*>(lds + p.lds_bits);  // [n * CHUNK / 32] sampled-key bitmap
+    double* cdfl = reinterpret_cast<double*>(lds + p.lds_cdf);       // [G][T + 1] chunk CDF C_t of each head
+    double* scl = reinterpret_cast<double*>(lds + p.lds_scl);        // [G][T] chunk scales exp(m_t - m*)
+    double* rows = reinterpret_cast<double*>(lds + p.lds_rows);      // [G][nb][CHUNK] prefix rows
     const int nbits = (n * CHUNK + 31) / 32;
-    for (int i = tid; i < n * CHUNK * NCW; i += STHREADS) cnt[i] = 0u;
-    for (int i = tid; i < nbits; i += STHREADS) bits[i] = 0u;
-    // the head of this wave: the exponential waves take heads 0..3, MFMA waves 0..3 heads 4..7
-    const int hw = (wave >= NMF && wave < NMF + SSOFT) ? wave - NMF : ((HG == 2 && wave < NMF) ? wave + 4 : -1);
+    for (int i = ttid; i < n * CHUNK * NCW; i += TT) cnt[i] = 0u;
+    for (int i = ttid; i < nbits; i += TT) bits[i] = 0u;
+    // the head of this wave: the exponential waves take heads 0..3 (whose prefix rows they hold), the copy
+    // waves heads 4..7
+    const int hw = tw < SSOFT ? tw : (HG == 2 ? tw - SSOFT + 4 : -1);
     const bool headwave = hw >= 0 && hw < G;
     const int64_t bhw = (int64_t)b * p.H + h0 + (headwave ? hw : 0);
     double* rowg = rows + (size_t)(headwave ? hw : 0) * LP.nb * CHUNK;
@@ -896,13 +905,12 @@ decode_tail: __attribute__((unused));
         // the candidate points of the batch's chunks, all at once: every point for i.i.d. sampling (its
         // chunk found among the batch's); for stratified / systematic sampling point m lies in
         // [m/S, (m+1)/S), so chunk t can only hold m in [floor(S C_t / Z) - 1, floor(S C_{t+1} / Z) + 1]
+        // (lane kk computes the range of chunk kb0 + kk)
         int clo[4], cpre[5];
-        cpre[0] = 0;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        {
           int lo = 0, np = 0;
-          if (kk < nbb && p.mode != 0) {
-            const int t = t0 + (kb0 + kk) * P;
+          if (lane < nbb && p.mode != 0) {
+            const int t = t0 + (kb0 + lane) * P;
             const double c0 = cg[t], c1 = cg[t + 1];
             if (c1 > c0 || t == lastc) {
               const double a = floor((double)p.S * (c0 * invZ)) - 1.0, e = floor((double)p.S * (c1 * invZ)) + 1.0;
@@ -912,8 +920,12 @@ decode_tail: __attribute__((unused));
               np = ihi >= ilo ? ihi - ilo + 1 : 0;
             }
           }
-          clo[kk] = lo;
-          cpre[kk + 1] = cpre[kk] + np;
+          cpre[0] = 0;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            clo[kk] = __builtin_amdgcn_readlane(lo, kk);
+            cpre[kk + 1] = cpre[kk] + __builtin_amdgcn_readlane(np, kk);
+          }
         }
         const int total = p.mode == 0 ? p.S : cpre[4];
         for (int c = lane; c < total; c += 64) {
@@ -958,7 +970,7 @@ decode_tail: __attribute__((unused));
     const bool good = !failed && dstat[0] == 0;  // block-uniform
 
     // -- compaction (one wave): the block's sampled keys in slot order, distinct keys per chunk
-    if (wave == 0) {
+    if (tw == 0) {
       int pc2[2], cw = 0;
       uint32_t wv[2];
 #pragma unroll
@@ -991,8 +1003,8 @@ decode_tail: __attribute__((unused));
     // -- gather: each sampled row of the block's chunks read once, count x row into fp32 per head
     constexpr int EPG = 4;              // elements per lane (8 bytes of bf16)
     constexpr int LPR = D / EPG;        // lanes per V row
-    constexpr int NRG = STHREADS / LPR; // rows per pass
-    const int rg = tid / LPR, pcl = tid % LPR;
+    constexpr int NRG = TT / LPR;       // rows per pass
+    const int rg = ttid / LPR, pcl = ttid % LPR;
     float acc[GM][EPG];
 #pragma unroll
     for (int g = 0; g < GM; ++g)
@@ -1046,7 +1058,7 @@ decode_tail: __attribute__((unused));
     __syncthreads();  // every wave is done with the counters and the list
     float* wsum = reinterpret_cast<float*>(lds);  // [NW * KEEP][GM][D]
     if (lane < LPR * KEEP) {
-      const int rgs = wave * KEEP + lane / LPR;
+      const int rgs = tw * KEEP + lane / LPR;
 #pragma unroll
       for (int g = 0; g < GM; ++g)
 #pragma unroll
@@ -1055,7 +1067,7 @@ decode_tail: __attribute__((unused));
     __syncthreads();
     const int GD = G * D;
     uint32_t* gpart = reinterpret_cast<uint32_t*>(p.partial) + (int64_t)me * GD;
-    for (int i = tid; i < GD; i += STHREADS) {
+    for (int i = ttid; i < GD; i += TT) {
       const int g = i / D, e = i % D;
       float sum = 0.0f;
 #pragma unroll
@@ -1073,7 +1085,7 @@ decode_tail: __attribute__((unused));
     float* fin = reinterpret_cast<float*>(lds);  // [P][no]
     const uint32_t* gparts = reinterpret_cast<const uint32_t*>(p.partial) + (int64_t)grp * P * GD + o0;
     bool fbad = false;
-    for (int j = tid; j < no * P; j += STHREADS) {
+    for (int j = ttid; j < no * P; j += TT) {
       const int i = j / no, e = j - i * no;
       const uint32_t* src = gparts + (int64_t)i * GD + e;
       uint32_t v = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1087,8 +1099,8 @@ decode_tail: __attribute__((unused));
     if (fbad) __hip_atomic_fetch_or(&dstat[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     __syncthreads();
     const bool poisoned = dstat[1] != 0;  // block-uniform
-    for (int e0 = tid >> 4; e0 < no; e0 += STHREADS / 16) {  // 16 threads per output, a fixed tree
-      const int q = tid & 15;
+    for (int e0 = ttid >> 4; e0 < no; e0 += TT / 16) {  // 16 threads per output, a fixed tree
+      const int q = ttid & 15;
       double sum = 0.0;
       for (int i = q; i < P; i += 16) sum += (double)fin[i * no + e0];
 #pragma unroll
@@ -1099,7 +1111,7 @@ decode_tail: __attribute__((unused));
         ((uint16_t*)p.out)[dst] = poisoned ? (uint16_t)0x7FC0u : f64_to_bf16_rne(sum / (double)p.S);
       }
     }
-    if (tid == 0) {
+    if (ttid == 0) {
       if (poisoned && (r == 0 || dstat[2] == 1))
         __hip_atomic_fetch_or(p.status + grp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       // block 0 has seen every block's partial words (its slice reads all P blocks), so every block of
