@@ -35,7 +35,7 @@ __device__ inline void piece_f32(const uint4& w, float* o) {
   }
 }
 
-// One block per (chunk of DENSE_CHUNK keys, KV head, sequence); each of the 4 waves owns 64 consecutive
+// One block per (chunk of DENSE_CHUNK keys, KV head, sequence); each of the 4 waves owns DENSE_CHUNK / 4 consecutive
 // keys of the chunk. LPR lanes hold one key row (16 bytes each), NRG rows side by side per load step. A
 // wave issues the K and V loads of up to RB rows per lane at once (V does not depend on the scores), then
 // keeps its own running max / sum-exp / weighted V sum, so the only block-wide step is the final merge of

@@ -51,7 +51,7 @@ struct DenseProblem {
   int Td;
   float* part;
 };
-constexpr int DENSE_CHUNK = 256;
+constexpr int DENSE_CHUNK = 128;  // keys per partial block (128 beat 256 and 64 in a sweep: more blocks, fewer registers)
 hipError_t launch_dense(const DenseProblem& p, hipStream_t st);
 
 // streaming read probe (util.hip): one XOR word per block into out[blocks]

@@ -684,6 +684,7 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   // ---- MFMA waves: 16-key groups x element parity = independent accumulation chains
   const int slot = lane >> 4;
   const int mh = wave / SPH, quart = wave % SPH;  // this wave's half of each chunk and key slice in it
+  if (mh == 1) __builtin_amdgcn_s_setprio(1);  // second halves land later and gate the next copies
   if constexpr (HG == 2) {
     for (int k = 0; k < n && ok; ++k) {
       const int jb = 2 * (k & 1) + mh;
