@@ -45,6 +45,14 @@ __device__ inline void copy_to_lds16(const void* g, uint32_t lds) {
                : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
+// one wave-wide 4-byte copy global -> LDS (lane l's dword at `g` lands at lds + 4 l): brings the line
+// of `g` into the caches without a register result
+__device__ inline void touch_to_lds4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // wait until at most N vector-memory operations of this wave are outstanding
@@ -291,6 +299,7 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   int* stc = &ctr[15];  // one-launch decode: the started flags of the group have been polled
   __shared__ int dstat[3];      // one-launch decode: statistics failed, output poisoned, started flags seen
   __shared__ uint64_t depoch;   // one-launch decode: the group's epoch at the start of this call
+  __shared__ uint32_t pfsink[DEC ? 64 : 1];  // one-launch decode: landing place of V-row prefetch copies
   __shared__ int wcnt[STHREADS / 64];
   double pv[NRX][4];            // one-launch decode, NREG > 0: this exponential wave's prefix rows
 
@@ -863,6 +872,8 @@ decode_tail: __attribute__((unused));
     // -- each head's chunk CDF from the group's statistics, then the points of the head that fall in this
     // block's chunks (one wave per head)
     int hst = 1;  // wave-uniform: 0 once this head wave's chunk CDF is in LDS
+    const int64_t vstride = 2 * p.seq_stride;
+    const char* vbase = (const char*)p.V + 2 * ((int64_t)b * p.batch_stride + (int64_t)kv * D);
     double2 zl = make_double2(0.0, 0.0);
     if (!failed && headwave) {
       double* cg = cdfl + (size_t)hw * (T + 1);
@@ -958,6 +969,11 @@ decode_tail: __attribute__((unused));
           if (j < 0) j = last_positive(rw, len);  // at or beyond the total through rounding
           j = min(j, len - 1);
           p.idx[bhw * p.S + m] = (int32_t)((int64_t)t * CHUNK + j);
+          // the key's V row, brought into the caches now for the gather below: copies into a sink in LDS
+          // that nothing reads, so nothing waits for them (the waves wait for their copies before ending)
+          const char* vrow = vbase + ((int64_t)t * CHUNK + j) * vstride;
+          touch_to_lds4(vrow, lds_addr(pfsink));
+          if constexpr (D * 2 > 128) touch_to_lds4(vrow + 128, lds_addr(pfsink));
           const int slot = k * CHUNK + j;
           atomicAdd(&cnt[slot * NCW + (g >> 1)], (g & 1) ? 0x10000u : 1u);
           atomicOr(&bits[slot >> 5], 1u << (slot & 31));
@@ -1104,8 +1120,10 @@ decode_tail: __attribute__((unused));
       const int q = ttid & 15;
       double sum = 0.0;
       for (int i = q; i < P; i += 16) sum += (double)fin[i * no + e0];
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
+      sum += dpp_f64<0xB1, 0xf>(0.0, sum);   // quad_perm [1,0,3,2]
+      sum += dpp_f64<0x4E, 0xf>(0.0, sum);   // quad_perm [2,3,0,1]
+      sum += dpp_f64<0x141, 0xf>(0.0, sum);  // row_half_mirror
+      sum += dpp_f64<0x140, 0xf>(0.0, sum);  // row_mirror
       if (q == 0) {
         const int o2 = o0 + e0, g = o2 / D, e = o2 % D;
         const int64_t dst = ((int64_t)b * p.H + h0 + g) * D + e;
@@ -1119,6 +1137,7 @@ decode_tail: __attribute__((unused));
       // the group has read the epoch: it may advance
       if (r == 0) __hip_atomic_store(p.sync_epoch + grp, depoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    wait_vm<0>();  // no V-row copy into the LDS sink may land after the block ends
   }
 }
 
