@@ -24,7 +24,7 @@ constexpr int64_t SEPARATE_CDF_MIN_BLOCKS = 2048;
 constexpr int SYNC_MAX_BLOCKS = 1024;
 constexpr int SYNC_MAX_GROUPS = 1024;
 constexpr int DECODE_MAX_T = 512;
-constexpr int DECODE_MAX_CHUNKS = 16;  // chunks per block: the sampled-key bitmap is scanned by one wave
+constexpr int DECODE_MAX_CHUNKS = 32;  // chunks per block: the sampled-key bitmap (4 words per lane) is scanned by one wave
 constexpr int SPIN_LIMIT_DEFAULT = 1 << 22;  // polls before a bounded wait gives up
 
 // ---------------------------------------------------------------------------------------------
@@ -298,6 +298,32 @@ __device__ inline double point_of(uint64_t seed, int mode, int S, int m, int h, 
   return ((double)m + u_sys) / (double)S;
 }
 
+// search_chunk (below) with three probes per round, a quarter of the interval left after each: fewer
+// dependent loads where P is in device memory.
+__device__ inline int search_chunk4(const double* P, double f, double r) {
+  int lo = 0, hi = CHUNK;  // answer in [lo, hi]
+  while (hi - lo > 4) {
+    const int s = (hi - lo) >> 2, q1 = lo + s, q2 = lo + 2 * s, q3 = lo + 3 * s;
+    const bool b1 = P[q1] * f > r, b2 = P[q2] * f > r, b3 = P[q3] * f > r;
+    if (b1) {
+      hi = q1;
+    } else if (b2) {
+      lo = q1 + 1;
+      hi = q2;
+    } else if (b3) {
+      lo = q2 + 1;
+      hi = q3;
+    } else {
+      lo = q3 + 1;
+    }
+  }
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (P[mid] * f > r) hi = mid; else lo = mid + 1;
+  }
+  return lo < CHUNK ? lo : -1;
+}
+
 // first j in [0, CHUNK) with P[j] * f > r, else -1 (P nondecreasing; entries past the chunk's last key
 // repeat the chunk total): the half-open inverse-CDF convention 1{F(j-1) <= t < F(j)} (Appendix A.4)
 __device__ inline int search_chunk(const double* P, double f, double r) {
@@ -423,9 +449,9 @@ struct Problem {
 
 // LDS plan of the sampling phase of the one-launch decode for G heads, n chunks per block and T chunks
 // per sequence, inside the `cap` bytes of the score phase's K tiles: per-key 16-bit counts per head, the
-// list and bitmap of the sampled keys, each head's chunk CDF C_0..C_T and chunk scales, and the prefix
-// rows of `nb` chunks per head at a time (nb = 0: does not fit). The same arithmetic on the host (which
-// picks the path) and in the kernel.
+// list and bitmap of the sampled keys, each head's chunk CDF C_0..C_T and chunk scales, and for G <= 4,
+// n <= 4 the prefix rows of the block's nb = n chunks per head (total = 0: does not fit). Computed on
+// the host, which passes the offsets to the kernel.
 struct DecodeLds {
   int nb;
   size_t cnt, list, bits, cdf, scl, rows, total;
@@ -439,11 +465,14 @@ __host__ __device__ inline DecodeLds decode_lds_plan(int G, int n, int T, size_t
   L.cdf = L.bits + ((size_t)n * CHUNK / 8 + 15) / 16 * 16;
   L.scl = L.cdf + ((size_t)G * (T + 1) * 8 + 15) / 16 * 16;
   L.rows = L.scl + (size_t)G * T * 8;
+  // the prefix rows go to LDS only where the score phase kept them in registers (G <= 4, n <= 4); with
+  // more chunks or heads they are searched where they are, in device memory
   const size_t per_chunk = (size_t)G * CHUNK * 8;
-  const size_t want_nb = n < 4 ? (size_t)n : 4;
+  const size_t want_nb = (G <= 4 && n <= 4) ? (size_t)n : 0;
   const size_t fit = cap > L.rows ? (cap - L.rows) / per_chunk : 0;
   L.nb = (int)(fit < want_nb ? fit : want_nb);
   L.total = L.rows + (size_t)L.nb * per_chunk;
+  if (L.nb < (int)want_nb || L.rows > cap) L.total = 0;  // does not fit
   return L;
 }
 

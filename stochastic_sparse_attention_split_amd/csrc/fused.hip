@@ -25,8 +25,7 @@ hipError_t launch_decode_d(const Problem& p, hipStream_t st, const LaunchEvents&
 // LDS the sampling phase of the one-launch decode needs for G heads, n chunks per block and T chunks per
 // sequence (0 if it does not fit the score phase's K tiles of head dimension d)
 size_t decode_lds_bytes(int G, int n, int T, int d) {
-  const DecodeLds L = decode_lds_plan(G, n, T, decode_lds_capacity(d));
-  return L.nb > 0 ? L.total : 0;
+  return decode_lds_plan(G, n, T, decode_lds_capacity(d)).total;
 }
 
 size_t decode_lds_capacity(int d) { return 2 * (size_t)CHUNK * d * 2; }

@@ -300,6 +300,9 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   __shared__ int dstat[3];      // one-launch decode: statistics failed, output poisoned, started flags seen
   __shared__ uint64_t depoch;   // one-launch decode: the group's epoch at the start of this call
   __shared__ uint32_t pfsink[DEC ? 64 : 1];  // one-launch decode: landing place of V-row prefetch copies
+  // one-launch decode, more than 4 chunks per block: first candidate point and exclusive prefix of the
+  // candidate counts of each chunk, per head
+  __shared__ int rlo[DEC ? 8 : 1][DEC ? DECODE_MAX_CHUNKS : 1], rpre[DEC ? 8 : 1][DEC ? DECODE_MAX_CHUNKS + 1 : 1];
   __shared__ int wcnt[STHREADS / 64];
   double pv[NRX][4];            // one-launch decode, NREG > 0: this exponential wave's prefix rows
 
@@ -826,7 +829,7 @@ decode_tail: __attribute__((unused));
     uint32_t* bits = reinterpret_cast<uint32_t*>(lds + p.lds_bits);  // [n * CHUNK / 32] sampled-key bitmap
     double* cdfl = reinterpret_cast<double*>(lds + p.lds_cdf);       // [G][T + 1] chunk CDF C_t of each head
     double* scl = reinterpret_cast<double*>(lds + p.lds_scl);        // [G][T] chunk scales exp(m_t - m*)
-    double* rows = reinterpret_cast<double*>(lds + p.lds_rows);      // [G][nb][CHUNK] prefix rows
+    double* rows = reinterpret_cast<double*>(lds + p.lds_rows);      // [G][nb][CHUNK] prefix rows (NREG > 0)
     const int nbits = (n * CHUNK + 31) / 32;
     for (int i = ttid; i < n * CHUNK * NCW; i += TT) cnt[i] = 0u;
     for (int i = ttid; i < nbits; i += TT) bits[i] = 0u;
@@ -835,30 +838,17 @@ decode_tail: __attribute__((unused));
     const int hw = tw < SSOFT ? tw : (HG == 2 ? tw - SSOFT + 4 : -1);
     const bool headwave = hw >= 0 && hw < G;
     const int64_t bhw = (int64_t)b * p.H + h0 + (headwave ? hw : 0);
-    double* rowg = rows + (size_t)(headwave ? hw : 0) * LP.nb * CHUNK;
-    // a batch of prefix rows (chunks kb0 ...) into this head's LDS rows: registers, or this CU's own stores
-    auto put_rows = [&](int kb0) {
-      const int nbb = min(LP.nb, n - kb0);
-      double v[4][4];
+    // the prefix rows of this head's chunks (at most 4), kept in the exponential wave's registers by the
+    // score phase, into LDS (with more chunks they stay in device memory, in this CU's L2)
+    auto put_rows = [&]() {
       if constexpr (NREG > 0) {
+        double* rowg = rows + (size_t)(headwave ? hw : 0) * LP.nb * CHUNK;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < NREG; ++kk)
+          if (kk < n)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[kk][i] = pv[kk < NREG ? kk : NREG - 1][i];
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {  // clamped to the batch's last chunk: every load is valid
-          const int t = t0 + (kb0 + min(kk, nbb - 1)) * P;
-          const double* src = p.stash + bhw * p.stash_stride + (int64_t)t * CHUNK + 4 * lane;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[kk][i] = src[i];
-        }
+            for (int i = 0; i < 4; ++i) rowg[kk * CHUNK + 4 * lane + i] = pv[kk][i];
       }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        if (kk < nbb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) rowg[kk * CHUNK + 4 * lane + i] = v[kk][i];
     };
 
     // a block whose score phase gave up publishes FAIL for its chunks, so no reader waits for them
@@ -866,7 +856,7 @@ decode_tail: __attribute__((unused));
       st_word(((lane & 1) ? p.csum : p.cmax) + bhw * T + t0 + (lane >> 1) * P, D_FAIL);
     const double u_sys =
         headwave && p.mode == 2 ? uniform53(p.seed, 0u, (uint32_t)(h0 + hw), (uint32_t)b, TAG_SYS) : 0.0;
-    if (headwave) put_rows(0);
+    if (headwave) put_rows();
     __syncthreads();  // the counters and the bitmap are clear
 
     // -- each head's chunk CDF from the group's statistics, then the points of the head that fall in this
@@ -900,87 +890,113 @@ decode_tail: __attribute__((unused));
       // (the products with 1/Z may round differently from the quotients; the +-1 margin of the candidate
       // range covers that, and each candidate is then tested exactly)
       const double invZ = 1.0 / Z;
-      for (int kb0 = 0; kb0 < n; kb0 += LP.nb) {
-        const int nbb = min(LP.nb, n - kb0);
-        if (kb0 > 0) put_rows(kb0);
+      if (__builtin_expect(p.prob != nullptr, 0)) {  // debug: probabilities from the score phase's exponentials
+        for (int kk = 0; kk < n; ++kk) {
+          const int t = t0 + kk * P, len = chunk_len(t);
+          const double f = sg[t];
+          double* prb = p.prob + bhw * p.nk + (int64_t)t * CHUNK;
+          for (int x = lane; x < len; x += 64) prb[x] = prb[x] * f / Z;
+        }
+      }
+      // the candidate points of the block's chunks, lane kk for chunk t0 + kk P: every point for i.i.d.
+      // sampling (its chunk found from the CDF); for stratified / systematic sampling point m lies in
+      // [m/S, (m+1)/S), so chunk t can only hold m in [floor(S C_t / Z) - 1, floor(S C_{t+1} / Z) + 1]
+      int lo = 0, np = 0;
+      if (lane < n && p.mode != 0) {
+        const int t = t0 + lane * P;
+        const double c0 = cg[t], c1 = cg[t + 1];
+        if (c1 > c0 || t == lastc) {
+          const double a = floor((double)p.S * (c0 * invZ)) - 1.0, e = floor((double)p.S * (c1 * invZ)) + 1.0;
+          const int ilo = (int)fmax(0.0, a);
+          const int ihi = t == lastc ? p.S - 1 : (int)fmin((double)(p.S - 1), e);
+          lo = ilo;
+          np = ihi >= ilo ? ihi - ilo + 1 : 0;
+        }
+      }
+      int clo[4], cpre[5];  // up to 4 chunks: in registers
+      cpre[0] = 0;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        clo[kk] = __builtin_amdgcn_readlane(lo, kk);
+        cpre[kk + 1] = cpre[kk] + __builtin_amdgcn_readlane(np, kk);
+      }
+      int total = p.mode == 0 ? p.S : cpre[4];
+      if (n > 4) {  // more chunks: first points and exclusive prefix of the counts in LDS (int DPP scan)
+        int incl = np;
+        incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xf, 0xf, false);  // row_shr:1
+        incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xf, 0xf, false);  // row_shr:2
+        incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xf, 0xf, false);  // row_shr:4
+        incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xf, 0xf, false);  // row_shr:8
+        incl += __builtin_amdgcn_update_dpp(0, incl, 0x142, 0xa, 0xf, false);  // row_bcast:15
+        incl += __builtin_amdgcn_update_dpp(0, incl, 0x143, 0xc, 0xf, false);  // row_bcast:31
+        if (lane < n) {
+          rlo[g][lane] = lo;
+          rpre[g][lane + 1] = incl;
+        }
+        if (lane == 0) rpre[g][0] = 0;
+        if (p.mode != 0) total = __builtin_amdgcn_readlane(incl, n - 1);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (p.prob) {  // debug: probabilities from the exponentials stored by the score phase
-          for (int kk = 0; kk < nbb; ++kk) {
-            const int t = t0 + (kb0 + kk) * P, len = chunk_len(t);
-            const double f = sg[t];
-            double* prb = p.prob + bhw * p.nk + (int64_t)t * CHUNK;
-            for (int x = lane; x < len; x += 64) prb[x] = prb[x] * f / Z;
-          }
-        }
-        // the candidate points of the batch's chunks, all at once: every point for i.i.d. sampling (its
-        // chunk found among the batch's); for stratified / systematic sampling point m lies in
-        // [m/S, (m+1)/S), so chunk t can only hold m in [floor(S C_t / Z) - 1, floor(S C_{t+1} / Z) + 1]
-        // (lane kk computes the range of chunk kb0 + kk)
-        int clo[4], cpre[5];
-        {
-          int lo = 0, np = 0;
-          if (lane < nbb && p.mode != 0) {
-            const int t = t0 + (kb0 + lane) * P;
-            const double c0 = cg[t], c1 = cg[t + 1];
-            if (c1 > c0 || t == lastc) {
-              const double a = floor((double)p.S * (c0 * invZ)) - 1.0, e = floor((double)p.S * (c1 * invZ)) + 1.0;
-              const int ilo = (int)fmax(0.0, a);
-              const int ihi = t == lastc ? p.S - 1 : (int)fmin((double)(p.S - 1), e);
-              lo = ilo;
-              np = ihi >= ilo ? ihi - ilo + 1 : 0;
-            }
-          }
-          cpre[0] = 0;
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            clo[kk] = __builtin_amdgcn_readlane(lo, kk);
-            cpre[kk + 1] = cpre[kk] + __builtin_amdgcn_readlane(np, kk);
-          }
-        }
-        const int total = p.mode == 0 ? p.S : cpre[4];
-        for (int c = lane; c < total; c += 64) {
-          int kk = 0, m = c;
-          if (p.mode != 0) {
+      }
+      for (int c = lane; c < total; c += 64) {
+        int k = 0, m = c;
+        if (p.mode != 0) {
+          if (n <= 4) {
 #pragma unroll
             for (int x = 1; x < 4; ++x)
-              if (c >= cpre[x]) kk = x;
-            m = clo[kk] + (c - cpre[kk]);
-          }
-          const double y = point_of(p.seed, p.mode, p.S, m, h, b, u_sys) * Z;
-          if (p.mode == 0) {  // the batch's chunk holding y, if any
-            kk = -1;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              if (x < nbb) {
-                const int t = t0 + (kb0 + x) * P;
-                if (y < Z ? (cg[t] <= y && y < cg[t + 1]) : (t == lastc)) kk = x;
-              }
+              if (c >= cpre[x]) k = x;
+            m = clo[k] + (c - cpre[k]);
+          } else {  // the last chunk whose first candidate is at or before c
+            int kl = 0, kh = n - 1;
+            while (kl < kh) {
+              const int mid = (kl + kh + 1) >> 1;
+              if (rpre[g][mid] <= c) kl = mid; else kh = mid - 1;
             }
-            if (kk < 0) continue;
+            k = kl;
+            m = rlo[g][k] + (c - rpre[g][k]);
           }
-          const int k = kb0 + kk, t = t0 + k * P, len = chunk_len(t);
-          const double c0 = cg[t], c1 = cg[t + 1];
-          const bool mine = y < Z ? (c0 <= y && y < c1) : (t == lastc);
-          if (!mine) continue;
-          const double* rw = rowg + kk * CHUNK;
-          int j = y < Z ? search_chunk(rw, sg[t], y - c0) : -1;
-          if (j < 0) j = last_positive(rw, len);  // at or beyond the total through rounding
-          j = min(j, len - 1);
-          p.idx[bhw * p.S + m] = (int32_t)((int64_t)t * CHUNK + j);
-          // the key's V row, brought into the caches now for the gather below: copies into a sink in LDS
-          // that nothing reads, so nothing waits for them (the waves wait for their copies before ending)
-          const char* vrow = vbase + ((int64_t)t * CHUNK + j) * vstride;
-          touch_to_lds4(vrow, lds_addr(pfsink));
-          if constexpr (D * 2 > 128) touch_to_lds4(vrow + 128, lds_addr(pfsink));
-          const int slot = k * CHUNK + j;
-          atomicAdd(&cnt[slot * NCW + (g >> 1)], (g & 1) ? 0x10000u : 1u);
-          atomicOr(&bits[slot >> 5], 1u << (slot & 31));
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // the rows are rewritten for the next batch
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const double y = point_of(p.seed, p.mode, p.S, m, h, b, u_sys) * Z;
+        if (p.mode == 0) {  // the chunk holding y, if it is one of this block's
+          int tt;
+          if (y < Z) {  // the last edge at or below y (edges are nondecreasing)
+            int el = 0, eh = T - 1;
+            while (el < eh) {
+              const int mid = (el + eh + 1) >> 1;
+              if (cg[mid] <= y) el = mid; else eh = mid - 1;
+            }
+            tt = el;
+          } else {
+            tt = lastc;
+          }
+          if (tt < t0 || (tt - t0) % P != 0) continue;
+          k = (tt - t0) / P;
+        }
+        const int t = t0 + k * P, len = chunk_len(t);
+        const double c0 = cg[t], c1 = cg[t + 1];
+        const bool mine = y < Z ? (c0 <= y && y < c1) : (t == lastc);
+        if (!mine) continue;
+        int j;
+        if constexpr (NREG > 0) {  // the block's prefix rows in LDS
+          const double* rw = rows + ((size_t)g * LP.nb + k) * CHUNK;
+          j = y < Z ? search_chunk(rw, sg[t], y - c0) : -1;
+          if (__builtin_expect(j < 0, 0)) j = last_positive(rw, len);  // at or beyond the total through rounding
+        } else {  // the block's own prefix rows in device memory (in its L2)
+          const double* rw = p.stash + bhw * p.stash_stride + (int64_t)t * CHUNK;
+          j = y < Z ? search_chunk4(rw, sg[t], y - c0) : -1;
+          if (__builtin_expect(j < 0, 0)) j = last_positive(rw, len);
+        }
+        j = min(j, len - 1);
+        p.idx[bhw * p.S + m] = (int32_t)((int64_t)t * CHUNK + j);
+        // the key's V row, brought into the caches now for the gather below: copies into a sink in LDS
+        // that nothing reads, so nothing waits for them (the waves wait for their copies before ending)
+        const char* vrow = vbase + ((int64_t)t * CHUNK + j) * vstride;
+        touch_to_lds4(vrow, lds_addr(pfsink));
+        if constexpr (D * 2 > 128) touch_to_lds4(vrow + 128, lds_addr(pfsink));
+        const int slot = k * CHUNK + j;
+        atomicAdd(&cnt[slot * NCW + (g >> 1)], (g & 1) ? 0x10000u : 1u);
+        atomicOr(&bits[slot >> 5], 1u << (slot & 31));
       }
     }
     __syncthreads();
@@ -988,30 +1004,35 @@ decode_tail: __attribute__((unused));
 
     // -- compaction (one wave): the block's sampled keys in slot order, distinct keys per chunk
     if (tw == 0) {
-      int pc2[2], cw = 0;
-      uint32_t wv[2];
+      int cw = 0;
+      uint32_t wv[4];  // bitmap words 4 lane .. 4 lane + 3 (at most 32 chunks of 8 words)
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int wi = 2 * lane + x;
+      for (int x = 0; x < 4; ++x) {
+        const int wi = 4 * lane + x;
         wv[x] = wi < nbits ? bits[wi] : 0u;
-        pc2[x] = __popc(wv[x]);
-        cw += pc2[x];
+        cw += __popc(wv[x]);
       }
-      const int incl = (int)wave_incl_scan_dpp((double)cw);  // small counts: exact in fp64
+      int incl = cw;  // inclusive prefix of the counts over the lanes (DPP row shifts and broadcasts)
+      incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xf, 0xf, false);
+      incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xf, 0xf, false);
+      incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xf, 0xf, false);
+      incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xf, 0xf, false);
+      incl += __builtin_amdgcn_update_dpp(0, incl, 0x142, 0xa, 0xf, false);
+      incl += __builtin_amdgcn_update_dpp(0, incl, 0x143, 0xc, 0xf, false);
       int pos = incl - cw;
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
+      for (int x = 0; x < 4; ++x) {
         uint32_t w = wv[x];
         while (w) {
-          list[pos++] = (2 * lane + x) * 32 + __builtin_ctz(w);
+          list[pos++] = (4 * lane + x) * 32 + __builtin_ctz(w);
           w &= w - 1u;
         }
       }
-      // chunk k owns words 8k .. 8k + 7, i.e. lanes 4k .. 4k + 3: its distinct keys are the scan's
-      // difference between lane 4k + 3 and lane 4k - 1
-      const int before4 = __shfl_up(incl, 4, 64);
-      if ((lane & 3) == 3 && lane / 4 < n)
-        p.unique[(int64_t)grp * T + t0 + (lane / 4) * P] = incl - (lane >= 4 ? before4 : 0);
+      // chunk k owns words 8k .. 8k + 7, i.e. lanes 2k and 2k + 1: its distinct keys are the scan's
+      // difference between lane 2k + 1 and lane 2k - 1
+      const int before2 = __shfl_up(incl, 2, 64);
+      if ((lane & 1) == 1 && lane / 2 < n)
+        p.unique[(int64_t)grp * T + t0 + (lane / 2) * P] = incl - (lane >= 2 ? before2 : 0);
       if (lane == 63) wcnt[0] = incl;
     }
     __syncthreads();

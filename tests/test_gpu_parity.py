@@ -543,6 +543,9 @@ ONE_LAUNCH_CASES = [
     (1, 28, 4, 128, 131072, "strat", 512, False, 40),  # G = 7, 512 chunks, 8 per block
     (3, 16, 8, 64, 25563, "strat", 64, True, 2),       # 24 groups, 10 chunks per block, ragged tail, ternary
     (1, 6, 2, 64, 777, "sys", 5, False, 1),            # 4 chunks, G = 3
+    (8, 32, 8, 128, 32768, "sys", 256, False, 4),      # 64 groups, 32 chunks per block (prefix rows in memory)
+    (4, 16, 4, 64, 40000, "iid", 128, False, 3),       # 16 groups, 10 chunks per block, i.i.d. (chunk from the CDF)
+    (2, 16, 2, 128, 20000, "strat", 96, False, 4),     # G = 8: heads 4..7 on the copy waves
 ]
 
 
