@@ -298,30 +298,27 @@ __device__ inline double point_of(uint64_t seed, int mode, int S, int m, int h, 
   return ((double)m + u_sys) / (double)S;
 }
 
-// search_chunk (below) with three probes per round, a quarter of the interval left after each: fewer
-// dependent loads where P is in device memory.
-__device__ inline int search_chunk4(const double* P, double f, double r) {
-  int lo = 0, hi = CHUNK;  // answer in [lo, hi]
-  while (hi - lo > 4) {
-    const int s = (hi - lo) >> 2, q1 = lo + s, q2 = lo + 2 * s, q3 = lo + 3 * s;
-    const bool b1 = P[q1] * f > r, b2 = P[q2] * f > r, b3 = P[q3] * f > r;
-    if (b1) {
-      hi = q1;
-    } else if (b2) {
-      lo = q1 + 1;
-      hi = q2;
-    } else if (b3) {
-      lo = q2 + 1;
-      hi = q3;
-    } else {
-      lo = q3 + 1;
-    }
-  }
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (P[mid] * f > r) hi = mid; else lo = mid + 1;
-  }
-  return lo < CHUNK ? lo : -1;
+// search_chunk (below) in two rounds of independent loads (fewer dependent round trips, in LDS or in
+// device memory): the first 16-entry block whose last entry exceeds r (15 probes), then the first
+// entry of that block that does.
+__device__ inline int search_chunk16(const double* P, double f, double r) {
+  static_assert(CHUNK == 256, "16 blocks of 16 entries");
+  double v[15];
+#pragma unroll
+  for (int i = 0; i < 15; ++i) v[i] = P[16 * i + 15];
+  int bi = 15;  // no earlier block qualifies: the answer, if any, is in the last one
+#pragma unroll
+  for (int i = 14; i >= 0; --i)
+    if (v[i] * f > r) bi = i;
+  double w[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) w[j] = P[16 * bi + j];
+  int j0 = 16;
+#pragma unroll
+  for (int j = 15; j >= 0; --j)
+    if (w[j] * f > r) j0 = j;
+  const int res = 16 * bi + j0;
+  return res < CHUNK ? res : -1;
 }
 
 // first j in [0, CHUNK) with P[j] * f > r, else -1 (P nondecreasing; entries past the chunk's last key

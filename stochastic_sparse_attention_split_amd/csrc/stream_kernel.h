@@ -977,16 +977,11 @@ decode_tail: __attribute__((unused));
         const double c0 = cg[t], c1 = cg[t + 1];
         const bool mine = y < Z ? (c0 <= y && y < c1) : (t == lastc);
         if (!mine) continue;
-        int j;
-        if constexpr (NREG > 0) {  // the block's prefix rows in LDS
-          const double* rw = rows + ((size_t)g * LP.nb + k) * CHUNK;
-          j = y < Z ? search_chunk(rw, sg[t], y - c0) : -1;
-          if (__builtin_expect(j < 0, 0)) j = last_positive(rw, len);  // at or beyond the total through rounding
-        } else {  // the block's own prefix rows in device memory (in its L2)
-          const double* rw = p.stash + bhw * p.stash_stride + (int64_t)t * CHUNK;
-          j = y < Z ? search_chunk4(rw, sg[t], y - c0) : -1;
-          if (__builtin_expect(j < 0, 0)) j = last_positive(rw, len);
-        }
+        // the block's prefix rows: in LDS (NREG > 0), else in its own stores in device memory (its L2)
+        const double* rw = NREG > 0 ? rows + ((size_t)g * LP.nb + k) * CHUNK
+                                    : p.stash + bhw * p.stash_stride + (int64_t)t * CHUNK;
+        int j = y < Z ? search_chunk16(rw, sg[t], y - c0) : -1;
+        if (__builtin_expect(j < 0, 0)) j = last_positive(rw, len);  // at or beyond the total through rounding
         j = min(j, len - 1);
         p.idx[bhw * p.S + m] = (int32_t)((int64_t)t * CHUNK + j);
         // the key's V row, brought into the caches now for the gather below: copies into a sink in LDS
