@@ -1,6 +1,6 @@
 // Dense decode attention baseline: softmax(q K^T / sqrt(dk)) V ("Stochastic Sparse Attention for
 // Memory-Bound Inference", Section 2, Eq. 1), split-KV like FlashDecoding: one block per (chunk of
-// DENSE_CHUNK keys, KV head, sequence) writes the chunk's (max, sum-exp, unnormalised output) for the G
+// dense_chunk(G) keys, KV head, sequence) writes the chunk's (max, sum-exp, unnormalised output) for the G
 // heads of the group; a merge block per (head, sequence) rescales and sums them. fp32 arithmetic on
 // bf16 or fp32 inputs; for bf16 the products use v_dot2 on bf16 pairs (the attention weights rounded to
 // bf16 for the V sum, as in FlashAttention-style kernels); reads all of K and V once.
@@ -35,7 +35,7 @@ __device__ inline void piece_f32(const uint4& w, float* o) {
   }
 }
 
-// One block per (chunk of DENSE_CHUNK keys, KV head, sequence); each of the 4 waves owns DENSE_CHUNK / 4 consecutive
+// One block per (chunk of CH keys, KV head, sequence); each of the 4 waves owns CH / 4 consecutive
 // keys of the chunk. LPR lanes hold one key row (16 bytes each), NRG rows side by side per load step. A
 // wave issues the K and V loads of up to RB rows per lane at once (V does not depend on the scores), then
 // keeps its own running max / sum-exp / weighted V sum, so the only block-wide step is the final merge of
@@ -71,12 +71,12 @@ __device__ inline float group_sum(float x) {
   return x;
 }
 
-template <int D, bool BF16, int GM>
+template <int D, bool BF16, int GM, int CH>
 __global__ __launch_bounds__(THREADS) void dense_partial_kernel(DenseProblem p) {
   constexpr int EPL = BF16 ? 8 : 4;        // elements per 16-byte piece
   constexpr int LPR = D / EPL;             // lanes per key row
   constexpr int NRG = 64 / LPR;            // rows per wave load step
-  constexpr int WROWS = DENSE_CHUNK / (THREADS / 64);
+  constexpr int WROWS = CH / (THREADS / 64);
   constexpr int R = WROWS / NRG;           // rows per lane
   constexpr int RBM = GM <= 4 ? 16 : 4;    // rows per lane in flight (fewer for 8 heads: registers)
   constexpr int RB = R < RBM ? R : RBM;
@@ -90,8 +90,8 @@ __global__ __launch_bounds__(THREADS) void dense_partial_kernel(DenseProblem p) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = p.G;
   const int rg = lane / LPR, pc = lane % LPR;
-  const int64_t n0 = (int64_t)t * DENSE_CHUNK;
-  const int len = (int)((p.nk - n0) < DENSE_CHUNK ? (p.nk - n0) : DENSE_CHUNK);
+  const int64_t n0 = (int64_t)t * CH;
+  const int len = (int)((p.nk - n0) < CH ? (p.nk - n0) : CH);
   const size_t esz = BF16 ? 2 : 4;
   const int64_t base = (int64_t)b * p.batch_stride + n0 * p.seq_stride + (int64_t)kv * D;
   const char* kb = (const char*)p.K + esz * base;
@@ -332,13 +332,13 @@ template <int D, bool BF16>
 hipError_t launch_dense_dt(const DenseProblem& p, hipStream_t st) {
   dim3 grid(p.Hkv, p.Td, p.B);
   if (p.G <= 1)
-    dense_partial_kernel<D, BF16, 1><<<grid, THREADS, 0, st>>>(p);
+    dense_partial_kernel<D, BF16, 1, dense_chunk(1)><<<grid, THREADS, 0, st>>>(p);
   else if (p.G <= 2)
-    dense_partial_kernel<D, BF16, 2><<<grid, THREADS, 0, st>>>(p);
+    dense_partial_kernel<D, BF16, 2, dense_chunk(2)><<<grid, THREADS, 0, st>>>(p);
   else if (p.G <= 4)
-    dense_partial_kernel<D, BF16, 4><<<grid, THREADS, 0, st>>>(p);
+    dense_partial_kernel<D, BF16, 4, dense_chunk(4)><<<grid, THREADS, 0, st>>>(p);
   else
-    dense_partial_kernel<D, BF16, 8><<<grid, THREADS, 0, st>>>(p);
+    dense_partial_kernel<D, BF16, 8, dense_chunk(8)><<<grid, THREADS, 0, st>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dense_merge_kernel<D, BF16><<<dim3(p.H, p.B, D / MCOLS), MERGE_THREADS, 0, st>>>(p);

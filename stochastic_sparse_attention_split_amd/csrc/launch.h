@@ -51,7 +51,11 @@ struct DenseProblem {
   int Td;
   float* part;
 };
-constexpr int DENSE_CHUNK = 128;  // keys per partial block (128 beat 256 and 64 in a sweep: more blocks, fewer registers)
+// keys per dense partial block: 128 for up to 4 heads per KV head (more blocks, fewer registers), 256 above
+// (the 8-head form keeps fewer rows in flight; smaller blocks only grow its merge) — the faster of 64,
+// 128 and 256 in a sweep on each form
+constexpr int dense_chunk(int G) { return G <= 4 ? 128 : 256; }
+constexpr int DENSE_CHUNK_MIN = 128;
 hipError_t launch_dense(const DenseProblem& p, hipStream_t st);
 
 // streaming read probe (util.hip): one XOR word per block into out[blocks]

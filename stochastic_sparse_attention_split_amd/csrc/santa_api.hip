@@ -535,7 +535,7 @@ void santa_release(void) {
 
 size_t santa_dense_workspace_bytes(int batch, int64_t nk, int heads, int kv_heads, int d) {
   if (batch < 1 || nk < 1 || heads < 1 || kv_heads < 1 || heads % kv_heads || (d != 64 && d != 128)) return 0;
-  const int64_t Td = (nk + DENSE_CHUNK - 1) / DENSE_CHUNK;
+  const int64_t Td = (nk + DENSE_CHUNK_MIN - 1) / DENSE_CHUNK_MIN;  // the most partials of any chunk size
   return align_up((size_t)(batch * (int64_t)heads * Td * (d + 2)) * sizeof(float));
 }
 
@@ -562,7 +562,8 @@ int santa_dense_decode(const santa_args* a) {
   p.batch_stride = bs;
   p.bf16 = a->dtype == SANTA_BF16;
   p.scale = (float)(1.0 / std::sqrt((double)a->d));
-  p.Td = (int)((a->nk + DENSE_CHUNK - 1) / DENSE_CHUNK);
+  const int ch = p.G <= 4 ? dense_chunk(4) : dense_chunk(8);
+  p.Td = (int)((a->nk + ch - 1) / ch);
   p.part = (float*)a->workspace;
   (void)hipGetLastError();
   const hipError_t e = launch_dense(p, (hipStream_t)a->stream);
