@@ -97,7 +97,9 @@ typedef struct santa_stats {
   int32_t launches;      /* kernels launched by the call */
   int64_t bytes_k;       /* K bytes streamed: batch * nk * kv_heads * d * elt (feature-major K: only the
                             feature rows read, sum over groups of rows * nk * elt) */
-  int64_t bytes_v;       /* V bytes gathered: (sum over (b, kv) of distinct sampled rows) * d * elt */
+  int64_t bytes_v;       /* V bytes gathered: (sum over (b, kv) of distinct sampled rows) * d * elt; in the
+                            two-launch S²ANTA-flash every head reads its own sampled rows of each tile, so
+                            there the sum runs over (b, head, tile) of that head's distinct rows in the tile */
   int64_t bytes_qo;      /* q read + out written: 2 * batch * heads * d * elt */
   int64_t unique_rows;   /* sum over (b, kv) of the distinct sampled rows */
   int64_t* group_unique_rows;  /* optional host array [batch * kv_heads] (NULL to skip): the distinct sampled

@@ -420,7 +420,7 @@ struct Problem {
   int32_t* lastpos;      // [B, H] last chunk with W_t > 0
   float* partial;        // [B, Hkv, T, G, d] per-chunk sums of count * V (fp32, exact products)
   int32_t* idx;          // [B, H, L]
-  int32_t* unique;       // [B, Hkv, T] distinct sampled keys of each chunk
+  int32_t* unique;       // [B, Hkv, T] distinct sampled keys of each chunk; then [B, Hkv, T] V rows read (fused flash)
   uint32_t* sink;        // [B, Hkv, T] values of the cache-warming loads (never read)
   int32_t* sync_err;     // [B, Hkv, T] per score block: 1 if an LDS handshake timed out
   int32_t* budget;       // [B, H, T] S²ANTA-prop tile budgets S_t

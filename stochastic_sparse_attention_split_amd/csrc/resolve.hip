@@ -755,18 +755,24 @@ __global__ __launch_bounds__(THREADS) void merge_flash_kernel(Problem p) {
     else
       ((float*)p.out)[o] = poisoned ? __uint_as_float(0x7FC00000u) : (float)r;
   }
-  if (p.fused && p.want_unique && g == 0) {  // distinct sampled keys per chunk: union of the heads' key bits
+  if (p.fused && p.want_unique && g == 0) {
+    // per chunk: distinct sampled keys (union of the heads' key bits) and V rows actually read (every head
+    // reads its own sampled rows, so the sum of the heads' bit counts), the latter after all B * Hkv * T
     const int grp = b * p.Hkv + kv;
     for (int t = tid; t < T; t += THREADS) {
       const uint64_t* bm = p.bmap + ((int64_t)grp * T + t) * 16;
-      int u = 0;
+      int u = 0, rd = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint64_t w = 0;
-        for (int gg = 0; gg < G; ++gg) w |= bm[gg * 4 + i];
+        for (int gg = 0; gg < G; ++gg) {
+          w |= bm[gg * 4 + i];
+          rd += __popcll(bm[gg * 4 + i]);
+        }
         u += __popcll(w);
       }
       p.unique[(int64_t)grp * T + t] = u;
+      p.unique[(int64_t)p.B * p.Hkv * T + (int64_t)grp * T + t] = rd;
     }
   }
   if (p.prob) {  // debug: probabilities from the score pass's exponentials, exp(s - m_t) exp(m_t - m*) / Z

@@ -73,7 +73,7 @@ Layout layout(int64_t B, int64_t nk, int64_t H, int64_t Hkv, int64_t d, int64_t 
   L.lastpos = take((size_t)(B * H) * sizeof(int32_t));
   L.partial = take((size_t)(B * Hkv * T * G * d) * sizeof(float));
   L.idx = take((size_t)(B * H * list_len(nk, (int)S, mode)) * sizeof(int32_t));
-  L.unique = take((size_t)(B * Hkv * T) * sizeof(int32_t));
+  L.unique = take((size_t)(2 * B * Hkv * T) * sizeof(int32_t));  // distinct keys, then rows read (fused flash)
   L.sink = take((size_t)(B * Hkv * T) * sizeof(uint32_t));
   L.sync_err = take((size_t)(B * Hkv * T) * sizeof(int32_t));
   L.budget = take((size_t)(B * H * T) * sizeof(int32_t));
@@ -352,6 +352,15 @@ int santa_decode_ex(const santa_args* a) {
     if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
     int64_t U = 0;
     for (int32_t x : u) U += x;
+    int64_t R = U;  // V rows read: each distinct row once per (sequence, KV head) ...
+    if (p.fused) {  // ... except in the fused S²ANTA-flash, where every head reads its own sampled rows
+      std::vector<int32_t> rd(u.size());
+      if ((e = hipMemcpy(rd.data(), p.unique + u.size(), rd.size() * sizeof(int32_t), hipMemcpyDeviceToHost)) !=
+          hipSuccess)
+        return hip_fail(e, "hipMemcpy(rows read)");
+      R = 0;
+      for (int32_t x : rd) R += x;
+    }
     const int64_t esz = p.bf16 ? 2 : 4;
     int64_t kbytes = (int64_t)a->batch * a->nk * a->kv_heads * a->d * esz;
     if (p.kfm) {  // feature rows actually read by the feature-major score pass
@@ -364,7 +373,7 @@ int santa_decode_ex(const santa_args* a) {
     santa_stats* s = a->stats_out;
     s->launches = p.one_launch ? 1 : (p.fused ? 2 : (cdf_kernel ? 4 : 3));
     s->bytes_k = kbytes;
-    s->bytes_v = U * a->d * esz;
+    s->bytes_v = R * a->d * esz;
     s->bytes_qo = 2 * (int64_t)a->batch * a->heads * a->d * esz;
     s->unique_rows = U;
     if (s->group_unique_rows)

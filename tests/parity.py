@@ -155,7 +155,16 @@ def compare(q, K, V, S, mode: str, seed: int, *, ternary=False, dtype="bf16", wa
         assert info["bytes_k"] == rows * Kn.shape[1] * esz, f"{label}: K bytes {info['bytes_k']} != {rows} rows"
     else:
         assert info["bytes_k"] == B * Kn.shape[1] * Kn.shape[2] * d * esz
-    assert info["bytes_v"] == info["unique_rows"] * d * esz
+    if mode == "flash" and info["launches"] == 2:
+        # fused S²ANTA-flash: each head reads its own distinct sampled rows of each tile (the GPU's samples)
+        St = int(r.extra["S_tile"])
+        tiles = np.sort(ig.reshape(B, H, -1, St), axis=-1)
+        read = int(tiles.shape[0] * tiles.shape[1] * tiles.shape[2] + (np.diff(tiles, axis=-1) != 0).sum())
+        assert read >= info["unique_rows"]
+        assert info["bytes_v"] == read * d * esz, f"{label}: V bytes {info['bytes_v']} != {read} rows read"
+        rep["rows_read"] = read
+    else:
+        assert info["bytes_v"] == info["unique_rows"] * d * esz
     assert info["launches"] >= 1
     rep["unique_rows"] = int(info["unique_rows"])
     return rep, r, out, idx
