@@ -94,13 +94,16 @@ __device__ inline int tile_off(int row, int pc) {
 }
 
 // Bounded poll of n flags in device memory (one wave; flags are read with coherent device-scope loads):
-// true once every flag equals `target`, false after `limit` checks. Up to 64 flags, four rounds of loads
-// stay in flight, spaced in time, each checked as it returns, so a flag is seen about a quarter of a
-// load's round trip after it lands rather than up to a whole round trip.
+// calls done(true) once every flag equals `target`, done(false) after `limit` checks. Up to 64 flags, four
+// rounds of loads stay in flight, spaced in time, each checked as it returns, so a flag is seen about a
+// quarter of a load's round trip after it lands rather than up to a whole round trip. The rounds still in
+// flight when the flags are seen are retired after done() (a use of their registers, so the compiler's
+// own wait lands there): code that joins this wave's path afterwards finds no load of it outstanding.
 __device__ inline uint64_t ld_flag(const uint64_t* f) {
   return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline bool poll_flags(const uint64_t* flags, int n, uint64_t target, int lane, int limit) {
+template <class Done>
+__device__ inline void poll_flags(const uint64_t* flags, int n, uint64_t target, int lane, int limit, Done&& done) {
   if (n <= 64) {
     const uint64_t* f = flags + (lane < n ? lane : n - 1);
     uint64_t v0 = ld_flag(f);
@@ -110,23 +113,26 @@ __device__ inline bool poll_flags(const uint64_t* flags, int n, uint64_t target,
     uint64_t v2 = ld_flag(f);
     __builtin_amdgcn_s_sleep(4);
     uint64_t v3 = ld_flag(f);
+    bool seen = false;
     for (int spins = 0; spins < limit; spins += 4) {
-      if (__ballot(v0 != target) == 0ull) return true;
+      if ((seen = __ballot(v0 != target) == 0ull)) break;
       v0 = ld_flag(f);
-      if (__ballot(v1 != target) == 0ull) return true;
+      if ((seen = __ballot(v1 != target) == 0ull)) break;
       v1 = ld_flag(f);
-      if (__ballot(v2 != target) == 0ull) return true;
+      if ((seen = __ballot(v2 != target) == 0ull)) break;
       v2 = ld_flag(f);
-      if (__ballot(v3 != target) == 0ull) return true;
+      if ((seen = __ballot(v3 != target) == 0ull)) break;
       v3 = ld_flag(f);
     }
-    return false;
+    done(seen);
+    asm volatile("" ::"v"(v0), "v"(v1), "v"(v2), "v"(v3));
+    return;
   }
   for (int spins = 0;; ++spins) {
     bool mine = true;
     for (int i = lane; i < n; i += 64) mine = (ld_flag(flags + i) == target) && mine;
-    if (__ballot(!mine) == 0ull) return true;
-    if (spins >= limit) return false;
+    if (__ballot(!mine) == 0ull) return done(true);
+    if (spins >= limit) return done(false);
     __builtin_amdgcn_s_sleep(1);
   }
 }
@@ -306,13 +312,28 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   __shared__ int wcnt[STHREADS / 64];
   double pv[NRX][4];            // one-launch decode, NREG > 0: this exponential wave's prefix rows
 
-  const int kv = blockIdx.y, b = blockIdx.z;
+  // (chunk slot, KV head, sequence) of this block. The one-launch decode numbers the blocks XCD by XCD:
+  // the dispatcher sends block l (in x, y, z order) to XCD l mod 8, so the blocks of a group share an
+  // XCD when its blocks fit in one, and their exchanges through device memory take the shorter trip
+  // (about 0.5 against 0.75 us per store-to-load hop, measured). Any placement gives the same results.
+  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+  if constexpr (DEC) {
+    const int nb = gridDim.x * gridDim.y * gridDim.z;
+    if ((nb & 7) == 0) {
+      const int l = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+      const int m = (l & 7) * (nb >> 3) + (l >> 3);
+      bx = m % gridDim.x;
+      by = (m / gridDim.x) % gridDim.y;
+      bz = m / (gridDim.x * gridDim.y);
+    }
+  }
+  const int kv = by, b = bz;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = p.G;
   const int h0 = kv * G;
   const int T = p.T;
   const int step = gridDim.x;
-  const int t0 = blockIdx.x;
+  const int t0 = bx;
   if (t0 >= T) return;
   const int n = (T - 1 - t0) / step + 1;  // this block's chunks: t0, t0 + step, ...
   int* err = p.sync_err + ((int64_t)b * gridDim.y + kv) * gridDim.x + t0;
@@ -421,10 +442,14 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
       if (!announced) announce();
       if (j == SCOPY - 1) {  // the started flags of the group, seen before the sampling phase needs them
         const uint64_t target = ((depoch + 1) << 10) | (uint64_t)grp;
-        bool seen = wait_ge(ivd, SCOPY, p.spin_limit);
-        seen = seen && poll_flags(p.sync_start + (int64_t)grp * step, step, target, lane, p.spin_limit);
-        if (lane == 0) dstat[2] = seen ? 1 : 2;
-        signal(stc, lane);
+        auto done = [&](bool seen) {
+          if (lane == 0) dstat[2] = seen ? 1 : 2;
+          signal(stc, lane);
+        };
+        if (wait_ge(ivd, SCOPY, p.spin_limit))
+          poll_flags(p.sync_start + (int64_t)grp * step, step, target, lane, p.spin_limit, done);
+        else
+          done(false);
       }
     }
     SK_PHASE1_DONE();
