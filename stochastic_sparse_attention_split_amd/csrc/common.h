@@ -366,6 +366,12 @@ __device__ inline double block_sum_f64(double v, double* red, int lane, int wave
   return r;
 }
 
+// a compile-time int as a value (selects a template instance inside a generic lambda)
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
 // element j (wave-uniform) of a small register array
 template <int N>
 __device__ inline double pick(const double* a, int j) {
@@ -374,6 +380,148 @@ __device__ inline double pick(const double* a, int j) {
   for (int i = 1; i < N; ++i)
     if (j == i) v = a[i];
   return v;
+}
+
+// S²ANTA-prop budgets of one head, computed by one wave (Appendix O, Algorithm 4; T <= 64 * PER, lane l
+// owns tiles [l*PER, l*PER + PER)): m* = max m_t, W_t = exp(m_t - m*) l_t, Z = sum W_t, q_t = S W_t / Z,
+// S_t = floor(q_t) plus one for the R = S - sum floor(q_t) largest fractional parts (ties to the lower
+// tile). The winners come from a radix select over the 80-bit keys (fraction bits, 0xFFFF - t), one byte
+// per pass, in a 256-bin LDS histogram owned by this wave; it stops once every key left in the chosen
+// bin wins. Gives every tile's S_t, its first slot sum_{t' < t} S_t', exp(m_t - m*), and Z.
+struct TileBudget {
+  int st, off;
+  double f, Z;
+};
+
+__device__ inline int prop_key_byte(uint64_t frac_bits, int t, int pass) {
+  return pass < 8 ? (int)((frac_bits >> (56 - 8 * pass)) & 255u)
+                  : (int)(((uint32_t)(0xFFFF - t) >> (8 * (9 - pass))) & 255u);
+}
+
+// every tile's values, each held by the lane that owns the tile
+template <int PER>
+struct TileBudgets {
+  double st[PER];   // S_t
+  double off[PER];  // first slot of the tile in the head's index list
+  double e[PER];    // exp(m_t - m*)
+  double Z;
+};
+
+template <int PER>
+__device__ inline void tile_budgets_wave(const double* m, const double* l, int T, int S, int lane, int* hist,
+                                         TileBudgets<PER>& o) {
+  const int t0 = lane * PER;
+  double mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (t0 + j < T) mx = fmax(mx, m[j]);
+  const double ms = readlane_f64(wave_incl_max_dpp(mx), 63);
+  double e[PER], w[PER], run = 0.0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    e[j] = exp_f64(m[j] - ms);
+    w[j] = t0 + j < T ? e[j] * l[j] : 0.0;
+    run += w[j];
+  }
+  const double Z = readlane_f64(wave_incl_scan_dpp(run), 63);
+  int fl[PER];
+  uint64_t key[PER];
+  uint32_t cand = 0u;
+  double flsum = 0.0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const double q = ((double)S * w[j]) / Z;
+    const double f = floor(q);
+    fl[j] = (int)f;
+    key[j] = (uint64_t)__double_as_longlong(q - f);
+    if (t0 + j < T) {
+      flsum += f;
+      cand |= 1u << j;
+    }
+  }
+  int need = S - (int)readlane_f64(wave_incl_scan_dpp(flsum), 63);
+  uint32_t above = 0u;
+  if (need > 0) {
+    for (int pass = 0; pass < 10; ++pass) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (cand >> j & 1u) atomicAdd(&hist[prop_key_byte(key[j], t0 + j, pass)], 1);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      int c[4], loc = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = hist[4 * lane + i];
+        loc += c[i];
+      }
+      const double incl = wave_incl_scan_dpp((double)loc);  // counts <= 64 * PER are exact
+      const int total = (int)readlane_f64(incl, 63);
+      int through = (int)incl - loc, sd = 0, sneed = 0, sbin = 0;
+      bool found = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        through += c[i];
+        const int hi = total - through;  // keys in higher bins
+        if (hi < need && need <= hi + c[i]) {
+          found = true;
+          sd = 4 * lane + i;
+          sneed = need - hi;
+          sbin = c[i];
+        }
+      }
+      const int owner = __builtin_ctzll(__ballot(found));  // exactly one lane finds the bin
+      const int d = __builtin_amdgcn_readlane(sd, owner), bin = __builtin_amdgcn_readlane(sbin, owner);
+      need = __builtin_amdgcn_readlane(sneed, owner);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        if (!(cand >> j & 1u)) continue;
+        const int kb = prop_key_byte(key[j], t0 + j, pass);
+        if (kb > d) above |= 1u << j;
+        if (kb != d) cand &= ~(1u << j);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // histogram reads done before the next clear
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (need == bin) break;  // wave-uniform; holds at the last pass, where every bin has one key
+    }
+    above |= cand;
+  }
+  double offv[PER], acc = 0.0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    o.st[j] = (double)(fl[j] + (int)(above >> j & 1u));
+    offv[j] = acc;  // local exclusive prefix
+    acc += t0 + j < T ? o.st[j] : 0.0;
+  }
+  const double inc = wave_incl_scan_dpp(acc);  // integer sums are exact in fp64
+  const double before = inc - acc;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    o.off[j] = before + offv[j];
+    o.e[j] = e[j];
+  }
+  o.Z = Z;
+}
+
+// the values of tile t (wave-uniform)
+template <int PER>
+__device__ inline TileBudget tile_budget_wave(const double* m, const double* l, int T, int S, int t, int lane,
+                                              int* hist) {
+  TileBudgets<PER> o;
+  tile_budgets_wave<PER>(m, l, T, S, lane, hist, o);
+  const int ol = t / PER, oj = t % PER;
+  TileBudget r;
+  r.st = (int)readlane_f64(pick<PER>(o.st, oj), ol);
+  r.off = (int)readlane_f64(pick<PER>(o.off, oj), ol);
+  r.f = readlane_f64(pick<PER>(o.e, oj), ol);
+  r.Z = o.Z;
+  return r;
 }
 
 // S²ANTA-flash uniform tile budget ("Stochastic Sparse Attention for Memory-Bound Inference", Appendix P,
@@ -441,7 +589,7 @@ struct Problem {
   uint64_t* sync_epoch;  // [SYNC_MAX_GROUPS]
   uint64_t* sync_start;  // [SYNC_MAX_BLOCKS] started flags: the block's published words are VOID
   bool one_launch;       // the whole decode runs in the score kernel
-  int lds_nb, lds_cnt, lds_list, lds_bits, lds_cdf, lds_scl, lds_rows;  // its sampling phase's LDS plan
+  int lds_nb, lds_cnt, lds_list, lds_bits, lds_cdf, lds_scl, lds_rows, lds_hist;  // its sampling phase's LDS plan
 };
 
 // LDS plan of the sampling phase of the one-launch decode for G heads, n chunks per block and T chunks
@@ -451,9 +599,10 @@ struct Problem {
 // the host, which passes the offsets to the kernel.
 struct DecodeLds {
   int nb;
-  size_t cnt, list, bits, cdf, scl, rows, total;
+  size_t cnt, list, bits, cdf, scl, rows, hist, total;
 };
-__host__ __device__ inline DecodeLds decode_lds_plan(int G, int n, int T, size_t cap) {
+// prop: S²ANTA-prop, whose head waves also need a 256-bin histogram each for the tile budgets
+__host__ __device__ inline DecodeLds decode_lds_plan(int G, int n, int T, size_t cap, bool prop) {
   const size_t gm = G <= 4 ? 4 : 8, ncw = gm / 2;
   DecodeLds L;
   L.cnt = 0;
@@ -468,14 +617,19 @@ __host__ __device__ inline DecodeLds decode_lds_plan(int G, int n, int T, size_t
   const size_t want_nb = (G <= 4 && n <= 4) ? (size_t)n : 0;
   const size_t fit = cap > L.rows ? (cap - L.rows) / per_chunk : 0;
   L.nb = (int)(fit < want_nb ? fit : want_nb);
-  L.total = L.rows + (size_t)L.nb * per_chunk;
-  if (L.nb < (int)want_nb || L.rows > cap) L.total = 0;  // does not fit
+  L.hist = L.rows + (size_t)L.nb * per_chunk;
+  L.total = L.hist + (prop ? gm * 256 * 4 : 0);
+  if (L.nb < (int)want_nb || L.total > cap) L.total = 0;  // does not fit
   return L;
 }
+
+// sampling modes, as numbered in the C header (SANTA_IID ... SANTA_FLASH)
+constexpr int MODE_IID = 0, MODE_STRAT = 1, MODE_SYS = 2, MODE_PROP = 3, MODE_FLASH = 4;
 
 // forms of the streaming score kernel
 constexpr int KM_SCORE = 0;   // scores, statistics and prefix rows for the separate sampling kernel
 constexpr int KM_FLASH = 1;   // S²ANTA-flash kernel 1 fused in
 constexpr int KM_DECODE = 2;  // the whole decode step in one launch
+constexpr int KM_DECODE_PROP = 3;  // the same for S²ANTA-prop (tile budgets and per-key counts, no points)
 
 }  // namespace santa

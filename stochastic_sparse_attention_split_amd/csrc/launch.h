@@ -35,7 +35,7 @@ hipError_t launch_merge(const Problem& p, hipStream_t st);     // resolve.hip: s
 // fused.hip: the whole decode in one launch (bf16, sequence-major K, G <= 8, T <= DECODE_MAX_T); grid
 // (score_blocks_per_group, Hkv, B), every block resident at once
 hipError_t launch_decode(const Problem& p, hipStream_t st, const LaunchEvents& ev = {});
-size_t decode_lds_bytes(int G, int n, int T, int d);  // LDS of its sampling phase (0: does not fit)
+size_t decode_lds_bytes(int G, int n, int T, int d, bool prop);  // LDS of its sampling phase (0: does not fit)
 size_t decode_lds_capacity(int d);       // LDS the score phase's K tiles provide
 
 // dense baseline (dense.hip): partials [B, H, Td, d + 2] fp32 then a merge

@@ -350,125 +350,6 @@ __global__ __launch_bounds__(THREADS) void resolve_kernel(Problem p) {
   if (lane == 0) p.sink[(int64_t)grp * T + t] = sink;  // keeps the cache-warming loads
 }
 
-// S²ANTA-prop budgets of one head, computed by one wave (Appendix O, Algorithm 4; T <= 64 * PER, lane l
-// owns tiles [l*PER, l*PER + PER)): m* = max m_t, W_t = exp(m_t - m*) l_t, Z = sum W_t, q_t = S W_t / Z,
-// S_t = floor(q_t) plus one for the R = S - sum floor(q_t) largest fractional parts (ties to the lower
-// tile). The winners come from a radix select over the 80-bit keys (fraction bits, 0xFFFF - t), one byte
-// per pass, in a 256-bin LDS histogram owned by this wave; it stops once every key left in the chosen
-// bin wins. Returns the values of tile `t`: S_t, its first slot sum_{t' < t} S_t', exp(m_t - m*), and Z.
-struct TileBudget {
-  int st, off;
-  double f, Z;
-};
-
-__device__ inline int prop_key_byte(uint64_t frac_bits, int t, int pass) {
-  return pass < 8 ? (int)((frac_bits >> (56 - 8 * pass)) & 255u)
-                  : (int)(((uint32_t)(0xFFFF - t) >> (8 * (9 - pass))) & 255u);
-}
-
-template <int PER>
-__device__ inline TileBudget tile_budget_wave(const double* m, const double* l, int T, int S, int t, int lane,
-                                              int* hist) {
-  const int t0 = lane * PER;
-  double mx = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if (t0 + j < T) mx = fmax(mx, m[j]);
-  const double ms = readlane_f64(wave_incl_max_dpp(mx), 63);
-  double e[PER], w[PER], run = 0.0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    e[j] = exp_f64(m[j] - ms);
-    w[j] = t0 + j < T ? e[j] * l[j] : 0.0;
-    run += w[j];
-  }
-  const double Z = readlane_f64(wave_incl_scan_dpp(run), 63);
-  int fl[PER];
-  uint64_t key[PER];
-  uint32_t cand = 0u;
-  double flsum = 0.0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const double q = ((double)S * w[j]) / Z;
-    const double f = floor(q);
-    fl[j] = (int)f;
-    key[j] = (uint64_t)__double_as_longlong(q - f);
-    if (t0 + j < T) {
-      flsum += f;
-      cand |= 1u << j;
-    }
-  }
-  int need = S - (int)readlane_f64(wave_incl_scan_dpp(flsum), 63);
-  uint32_t above = 0u;
-  if (need > 0) {
-    for (int pass = 0; pass < 10; ++pass) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int j = 0; j < PER; ++j)
-        if (cand >> j & 1u) atomicAdd(&hist[prop_key_byte(key[j], t0 + j, pass)], 1);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      int c[4], loc = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c[i] = hist[4 * lane + i];
-        loc += c[i];
-      }
-      const double incl = wave_incl_scan_dpp((double)loc);  // counts <= 64 * PER are exact
-      const int total = (int)readlane_f64(incl, 63);
-      int through = (int)incl - loc, sd = 0, sneed = 0, sbin = 0;
-      bool found = false;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        through += c[i];
-        const int hi = total - through;  // keys in higher bins
-        if (hi < need && need <= hi + c[i]) {
-          found = true;
-          sd = 4 * lane + i;
-          sneed = need - hi;
-          sbin = c[i];
-        }
-      }
-      const int owner = __builtin_ctzll(__ballot(found));  // exactly one lane finds the bin
-      const int d = __builtin_amdgcn_readlane(sd, owner), bin = __builtin_amdgcn_readlane(sbin, owner);
-      need = __builtin_amdgcn_readlane(sneed, owner);
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        if (!(cand >> j & 1u)) continue;
-        const int kb = prop_key_byte(key[j], t0 + j, pass);
-        if (kb > d) above |= 1u << j;
-        if (kb != d) cand &= ~(1u << j);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // histogram reads done before the next clear
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      if (need == bin) break;  // wave-uniform; holds at the last pass, where every bin has one key
-    }
-    above |= cand;
-  }
-  double stv[PER], offv[PER], acc = 0.0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    stv[j] = (double)(fl[j] + (int)(above >> j & 1u));
-    offv[j] = acc;  // local exclusive prefix
-    acc += t0 + j < T ? stv[j] : 0.0;
-  }
-  const double inc = wave_incl_scan_dpp(acc);  // integer sums are exact in fp64
-  const double before = inc - acc;
-  const int ol = t / PER, oj = t % PER;
-  TileBudget r;
-  r.st = (int)readlane_f64(pick<PER>(stv, oj), ol);
-  r.off = (int)readlane_f64(before + pick<PER>(offv, oj), ol);
-  r.f = readlane_f64(pick<PER>(e, oj), ol);
-  r.Z = Z;
-  return r;
-}
-
 // S²ANTA-prop, pass 2 (Appendix O, Algorithm 5): the chunk (= tile) of each head has budget S_t; with
 // x_n = (S_t / l_t) u_n and a0 ~ U(0,1) from Philox counter (t, h, b, 3), key n of the tile is sampled
 // c_n = floor(a0 + P_n) - floor(a0 + P_{n-1}) times, P_n = (S_t / l_t) * (in-chunk prefix of u up to n)

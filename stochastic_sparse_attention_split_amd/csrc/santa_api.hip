@@ -176,18 +176,22 @@ int score_blocks_per_group(int groups, int T, int per_cu) {
   return per < 1 ? 1 : (per > T ? T : per);
 }
 
+static_assert(MODE_IID == SANTA_IID && MODE_STRAT == SANTA_STRAT && MODE_SYS == SANTA_SYS &&
+                  MODE_PROP == SANTA_PROP && MODE_FLASH == SANTA_FLASH,
+              "the kernels number the sampling modes as the C header does");
+
 // The one-launch decode applies when the streaming score kernel runs (bf16, sequence-major K, G <= 8), the
-// sampling is i.i.d., stratified or systematic, every block of the grid fits on the device at once (one
-// per CU), the chunk CDF fits the in-kernel form and the sampling phase's LDS fits the K tiles. Returns
-// the blocks per group, or 0 when the multi-launch path runs.
+// sampling is i.i.d., stratified, systematic or S²ANTA-prop, every block of the grid fits on the device at
+// once (one per CU), the chunk CDF fits the in-kernel form and the sampling phase's LDS fits the K tiles.
+// Returns the blocks per group, or 0 when the multi-launch path runs.
 int one_launch_blocks(const Problem& p, int cus) {
-  if (!p.bf16 || p.kfm || p.group_bern || p.mode > SANTA_SYS || p.G > MAX_GROUP || p.T > DECODE_MAX_T) return 0;
+  if (!p.bf16 || p.kfm || p.group_bern || p.mode > SANTA_PROP || p.G > MAX_GROUP || p.T > DECODE_MAX_T) return 0;
   const int groups = p.B * p.Hkv;
   if (groups > cus || groups > SYNC_MAX_GROUPS) return 0;
   const int per = std::min(p.T, cus / groups);
   if ((int64_t)per * groups > SYNC_MAX_BLOCKS) return 0;
   const int n = (p.T + per - 1) / per;
-  if (n > DECODE_MAX_CHUNKS || decode_lds_bytes(p.G, n, p.T, p.d) == 0) return 0;
+  if (n > DECODE_MAX_CHUNKS || decode_lds_bytes(p.G, n, p.T, p.d, p.mode == SANTA_PROP) == 0) return 0;
   if (p.mode == SANTA_IID && (int64_t)n * p.S > 32768) return 0;  // i.i.d. points are tested in every chunk
   return per;
 }
@@ -299,7 +303,8 @@ int santa_decode_ex(const santa_args* a) {
   if (p.one_launch) {
     p.score_blocks_per_group = one;
     // the sampling phase's LDS plan for the largest chunk count of a block (checked to fit above)
-    const DecodeLds L = decode_lds_plan(p.G, (p.T + one - 1) / one, p.T, decode_lds_capacity(p.d));
+    const DecodeLds L =
+        decode_lds_plan(p.G, (p.T + one - 1) / one, p.T, decode_lds_capacity(p.d), p.mode == SANTA_PROP);
     p.lds_nb = L.nb;
     p.lds_cnt = (int)L.cnt;
     p.lds_list = (int)L.list;
@@ -307,6 +312,7 @@ int santa_decode_ex(const santa_args* a) {
     p.lds_cdf = (int)L.cdf;
     p.lds_scl = (int)L.scl;
     p.lds_rows = (int)L.rows;
+    p.lds_hist = (int)L.hist;
   }
 
   hipStream_t stream = (hipStream_t)a->stream;

@@ -3,8 +3,9 @@
 //   KM_SCORE:  scores, chunk statistics and the in-chunk prefix rows ("stash") for the sampling kernel;
 //   KM_FLASH:  S²ANTA-flash kernel 1 fused in (samples and gathers each tile right after its exponentials);
 //   KM_DECODE: the whole decode step in one launch: after the score phase the blocks of a (KV head,
-//              sequence) group meet at a barrier, then every block samples and gathers its own chunks and
-//              the group's output is summed (the tail of score_stream_kernel).
+//              sequence) group exchange their chunk statistics, then every block samples and gathers its
+//              own chunks and the group's output is summed (the tail of score_stream_kernel);
+//   KM_DECODE_PROP: the same for S²ANTA-prop (tile budgets and per-key counts instead of points).
 #pragma once
 
 #include "common.h"
@@ -154,11 +155,12 @@ __device__ inline void st_word(double* f, uint64_t v) {
 // One-launch decode: the chunk CDF of one head (Appendix O, Algorithm 4) from the chunk statistics the
 // blocks of its group publish: loads every word once, then reloads (bounded) the words still VOID; lane
 // l owns chunks [l PER, (l + 1) PER). The
-// edges C_0..C_T and the chunk scales exp(m_t - m*) go to LDS (cg, sg) and (Z, last chunk with mass) to
-// zl. Returns 0, or 1 if a block reported FAIL or the wait gave up.
+// edges C_0..C_T and the chunk scales exp(m_t - m*) go to LDS (cg, sg), (Z, last chunk with mass) to
+// zl, and the lane's statistics m_t, l_t to mo, lo. Returns 0, or 1 if a block reported FAIL or the wait
+// gave up.
 template <int PER>
 __device__ inline int cdf_poll_to_lds(const double* cm, const double* cs, int T, int lane, int limit,
-                                      double* cg, double* sg, double2* zl) {
+                                      double* cg, double* sg, double2* zl, double* mo, double* lo) {
   uint64_t wm[PER], wl[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {  // lanes past T re-read the last chunk
@@ -189,6 +191,11 @@ __device__ inline int cdf_poll_to_lds(const double* cm, const double* cs, int T,
     l[j] = __longlong_as_double((long long)wl[j]);
   }
   if (__ballot(fl) != 0ull) return 1;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    mo[j] = m[j];
+    lo[j] = l[j];
+  }
   ChunkCdf<PER> o;
   chunk_cdf_wave<PER>(m, l, T, lane, o);
 #pragma unroll
@@ -265,13 +272,14 @@ __device__ inline bool wait_ge(int* ctr, int target, int limit) {
     }                           \
   } while (0)
 
-// KM_DECODE: the whole decode step in one launch; NREG > 0 keeps each exponential wave's prefix rows of
+// KM_DECODE(_PROP): the whole decode step in one launch; NREG > 0 keeps each exponential wave's prefix rows of
 // the block's (at most NREG) chunks in registers instead of storing them (G <= 4). The sampling and
 // gather phase after the score phase is described at the start of that phase (decode_tail) below.
 template <int D, int HG, int KM, int NREG = 0>
 __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   constexpr bool FL = KM == KM_FLASH;
-  constexpr bool DEC = KM == KM_DECODE;
+  constexpr bool DEC = KM == KM_DECODE || KM == KM_DECODE_PROP;
+  constexpr bool DPROP = KM == KM_DECODE_PROP;
   static_assert(!FL || HG == 1, "the fused S²ANTA-flash form covers G <= 4");
   static_assert(NREG == 0 || (DEC && HG == 1), "register prefix rows: one-launch decode with G <= 4");
   constexpr int NRX = NREG > 0 ? NREG : 1;
@@ -890,6 +898,48 @@ decode_tail: __attribute__((unused));
     const int64_t vstride = 2 * p.seq_stride;
     const char* vbase = (const char*)p.V + 2 * ((int64_t)b * p.batch_stride + (int64_t)kv * D);
     double2 zl = make_double2(0.0, 0.0);
+    // S²ANTA-prop ("Stochastic Sparse Attention for Memory-Bound Inference", Section 3.2; Appendix O,
+    // Algorithms 4 and 5): the head's tile budgets S_t from every chunk's statistics (largest remainder,
+    // the multi-launch path's own code), then for each of the block's chunks with S_t > 0 the systematic
+    // counts c_n = floor(a0 + P_n S_t / l_t) - floor(a0 + P_{n-1} S_t / l_t) of its keys (lane l: keys
+    // 4 l .. 4 l + 3, P the in-chunk prefix), their slots [first slot of the tile + floor(..)) in the
+    // head's index list, and their counts and key bits for the gather. The outputs are (1/S) sum c_n v_n.
+    auto prop_counts = [&](auto per, const double* mo, const double* lo) {
+      constexpr int PER = decltype(per)::value;
+      TileBudgets<PER> tb;
+      tile_budgets_wave<PER>(mo, lo, T, p.S, lane, reinterpret_cast<int*>(lds + p.lds_hist) + hw * 256, tb);
+      const int g = hw, h = h0 + hw;
+      for (int k = 0; k < n; ++k) {
+        const int t = t0 + k * P, len = chunk_len(t);
+        const int ol = t / PER, oj = t % PER;
+        const int st = (int)readlane_f64(pick<PER>(tb.st, oj), ol);
+        if (st == 0) continue;  // wave-uniform
+        const int off = (int)readlane_f64(pick<PER>(tb.off, oj), ol);
+        const double inv = (double)st / readlane_f64(pick<PER>(lo, oj), ol);
+        const double a0 = uniform53(p.seed, (uint32_t)t, (uint32_t)h, (uint32_t)b, TAG_PROP);
+        const double* rw = NREG > 0 ? rows + ((size_t)g * LP.nb + k) * CHUNK
+                                    : p.stash + bhw * p.stash_stride + (int64_t)t * CHUNK;
+        int32_t* dst = p.idx + bhw * p.L + off;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int x = 4 * lane + i;
+          if (x >= len) continue;
+          const double ylo = a0 + inv * (x > 0 ? rw[x - 1] : 0.0);
+          const double yhi = a0 + inv * rw[x];
+          const int lo_ = (int)floor(ylo), hi_ = (int)floor(yhi);
+          const int c = hi_ > lo_ ? min(hi_ - lo_, st) : 0;
+          if (c == 0) continue;
+          for (int q = 0; q < c; ++q)  // slots outside the tile's budget are never written
+            if (lo_ + q >= 0 && lo_ + q < st) dst[lo_ + q] = (int32_t)((int64_t)t * CHUNK + x);
+          const char* vrow = vbase + ((int64_t)t * CHUNK + x) * vstride;  // into the caches for the gather
+          touch_to_lds4(vrow, lds_addr(pfsink));
+          if constexpr (D * 2 > 128) touch_to_lds4(vrow + 128, lds_addr(pfsink));
+          const int slot = k * CHUNK + x;
+          atomicAdd(&cnt[slot * NCW + (g >> 1)], (g & 1) ? ((uint32_t)c << 16) : (uint32_t)c);
+          atomicOr(&bits[slot >> 5], 1u << (slot & 31));
+        }
+      }
+    };
     if (!failed && headwave) {
       double* cg = cdfl + (size_t)hw * (T + 1);
       double* sg = scl + (size_t)hw * T;
@@ -899,10 +949,19 @@ decode_tail: __attribute__((unused));
         // for this T (the same edges, bit for bit)
         const double* cmg = p.cmax + bhw * T;
         const double* csg = p.csum + bhw * T;
-        if (T <= 64) hst = cdf_poll_to_lds<1>(cmg, csg, T, lane, p.spin_limit, cg, sg, &zl);
-        else if (T <= 128) hst = cdf_poll_to_lds<2>(cmg, csg, T, lane, p.spin_limit, cg, sg, &zl);
-        else if (T <= 256) hst = cdf_poll_to_lds<4>(cmg, csg, T, lane, p.spin_limit, cg, sg, &zl);
-        else hst = cdf_poll_to_lds<8>(cmg, csg, T, lane, p.spin_limit, cg, sg, &zl);
+        auto poll = [&](auto per) {
+          constexpr int PER = decltype(per)::value;
+          double mo[PER], lo[PER];
+          const int r = cdf_poll_to_lds<PER>(cmg, csg, T, lane, p.spin_limit, cg, sg, &zl, mo, lo);
+          if constexpr (DPROP) {
+            if (r == 0) prop_counts(per, mo, lo);
+          }
+          return r;
+        };
+        if (T <= 64) hst = poll(IntC<1>());
+        else if (T <= 128) hst = poll(IntC<2>());
+        else if (T <= 256) hst = poll(IntC<4>());
+        else hst = poll(IntC<8>());
       }
       if (hst != 0 && lane == 0) __hip_atomic_fetch_or(&dstat[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
@@ -927,7 +986,7 @@ decode_tail: __attribute__((unused));
       // sampling (its chunk found from the CDF); for stratified / systematic sampling point m lies in
       // [m/S, (m+1)/S), so chunk t can only hold m in [floor(S C_t / Z) - 1, floor(S C_{t+1} / Z) + 1]
       int lo = 0, np = 0;
-      if (lane < n && p.mode != 0) {
+      if (lane < n && p.mode != 0 && !DPROP) {  // (S²ANTA-prop has no points)
         const int t = t0 + lane * P;
         const double c0 = cg[t], c1 = cg[t + 1];
         if (c1 > c0 || t == lastc) {

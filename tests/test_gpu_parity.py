@@ -546,6 +546,12 @@ ONE_LAUNCH_CASES = [
     (8, 32, 8, 128, 32768, "sys", 256, False, 4),      # 64 groups, 32 chunks per block (prefix rows in memory)
     (4, 16, 4, 64, 40000, "iid", 128, False, 3),       # 16 groups, 10 chunks per block, i.i.d. (chunk from the CDF)
     (2, 16, 2, 128, 20000, "strat", 96, False, 4),     # G = 8: heads 4..7 on the copy waves
+    (1, 32, 8, 128, 32768, "prop", 128, False, 32),    # S²ANTA-prop at its 32k operating point
+    (1, 4, 1, 128, 30000, "prop", 200, False, 8),      # S²ANTA-prop, one chunk per block
+    (2, 16, 2, 128, 60000, "prop", 64, False, 6),      # S²ANTA-prop, 235 tiles: budgets by the budget kernel
+    (1, 28, 4, 128, 131072, "prop", 512, False, 40),   # S²ANTA-prop, G = 7, 512 tiles, 8 per block
+    (2, 16, 2, 128, 20000, "prop", 96, False, 4),      # S²ANTA-prop, G = 8
+    (3, 16, 8, 64, 25563, "prop", 64, True, 2),        # S²ANTA-prop, d = 64, ragged tail, ternary
 ]
 
 
@@ -553,7 +559,8 @@ ONE_LAUNCH_CASES = [
                          ids=[f"B{c[0]}H{c[1]}kv{c[2]}d{c[3]}n{c[4]}{c[5]}S{c[6]}" for c in ONE_LAUNCH_CASES])
 def test_one_launch_matches_multi_launch(case):
     """The one-launch decode (one kernel) and the multi-launch path (score, sampling, merge kernels) take
-    the same indices; their outputs differ only in the grouping of the fp32 partial sums."""
+    the same indices; their outputs differ only in the grouping of the fp32 partial sums (S²ANTA-prop:
+    the same tile budgets, whether a wave of the decode kernel or the separate budget kernel forms them)."""
     B, H, Hkv, d, nk, mode, S, tern, spikes = case
     log(f"one launch vs multi launch {case}")
     dev = torch.device("cuda:0")
