@@ -366,6 +366,17 @@ __device__ inline double block_sum_f64(double v, double* red, int lane, int wave
   return r;
 }
 
+// inclusive prefix sum of an int over the wave (DPP row shifts and broadcasts)
+__device__ inline int wave_incl_scan_i32(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
 // a compile-time int as a value (selects a template instance inside a generic lambda)
 template <int N>
 struct IntC {
@@ -442,7 +453,17 @@ __device__ inline void tile_budgets_wave(const double* m, const double* l, int T
   int need = S - (int)readlane_f64(wave_incl_scan_dpp(flsum), 63);
   uint32_t above = 0u;
   if (need > 0) {
-    for (int pass = 0; pass < 10; ++pass) {
+    // a byte that every key shares would put every candidate in one bin and change nothing: the passes
+    // start at the first byte in which the keys differ (the tile bytes if every fraction is equal)
+    const uint64_t ref = (uint64_t)__shfl((long long)key[0], 0, 64);  // tile 0 always exists
+    uint64_t dif = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (cand >> j & 1u) dif |= key[j] ^ ref;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) dif |= (uint64_t)__shfl_xor((long long)dif, o, 64);
+    const int first = dif == 0 ? 8 : __builtin_clzll(dif) / 8;
+    for (int pass = first; pass < 10; ++pass) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -460,9 +481,9 @@ __device__ inline void tile_budgets_wave(const double* m, const double* l, int T
         c[i] = hist[4 * lane + i];
         loc += c[i];
       }
-      const double incl = wave_incl_scan_dpp((double)loc);  // counts <= 64 * PER are exact
-      const int total = (int)readlane_f64(incl, 63);
-      int through = (int)incl - loc, sd = 0, sneed = 0, sbin = 0;
+      const int incl = wave_incl_scan_i32(loc);
+      const int total = __builtin_amdgcn_readlane(incl, 63);
+      int through = incl - loc, sd = 0, sneed = 0, sbin = 0;
       bool found = false;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {

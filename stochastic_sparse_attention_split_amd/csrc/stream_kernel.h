@@ -156,9 +156,9 @@ __device__ inline void st_word(double* f, uint64_t v) {
 // blocks of its group publish: loads every word once, then reloads (bounded) the words still VOID; lane
 // l owns chunks [l PER, (l + 1) PER). The
 // edges C_0..C_T and the chunk scales exp(m_t - m*) go to LDS (cg, sg), (Z, last chunk with mass) to
-// zl, and the lane's statistics m_t, l_t to mo, lo. Returns 0, or 1 if a block reported FAIL or the wait
-// gave up.
-template <int PER>
+// zl, and the lane's statistics m_t, l_t to mo, lo (without the CDF if CDF is false). Returns 0, or 1 if
+// a block reported FAIL or the wait gave up.
+template <int PER, bool CDF = true>
 __device__ inline int cdf_poll_to_lds(const double* cm, const double* cs, int T, int lane, int limit,
                                       double* cg, double* sg, double2* zl, double* mo, double* lo) {
   uint64_t wm[PER], wl[PER];
@@ -196,6 +196,7 @@ __device__ inline int cdf_poll_to_lds(const double* cm, const double* cs, int T,
     mo[j] = m[j];
     lo[j] = l[j];
   }
+  if constexpr (!CDF) return 0;
   ChunkCdf<PER> o;
   chunk_cdf_wave<PER>(m, l, T, lane, o);
 #pragma unroll
@@ -912,6 +913,10 @@ decode_tail: __attribute__((unused));
       for (int k = 0; k < n; ++k) {
         const int t = t0 + k * P, len = chunk_len(t);
         const int ol = t / PER, oj = t % PER;
+        if (__builtin_expect(p.prob != nullptr, 0)) {  // for the debug probabilities below
+          const double et = readlane_f64(pick<PER>(tb.e, oj), ol);  // (every lane forms its pick first)
+          if (lane == 0) scl[(size_t)g * T + t] = et;
+        }
         const int st = (int)readlane_f64(pick<PER>(tb.st, oj), ol);
         if (st == 0) continue;  // wave-uniform
         const int off = (int)readlane_f64(pick<PER>(tb.off, oj), ol);
@@ -929,8 +934,9 @@ decode_tail: __attribute__((unused));
           const int lo_ = (int)floor(ylo), hi_ = (int)floor(yhi);
           const int c = hi_ > lo_ ? min(hi_ - lo_, st) : 0;
           if (c == 0) continue;
-          for (int q = 0; q < c; ++q)  // slots outside the tile's budget are never written
-            if (lo_ + q >= 0 && lo_ + q < st) dst[lo_ + q] = (int32_t)((int64_t)t * CHUNK + x);
+          if (p.want_idx)
+            for (int q = 0; q < c; ++q)  // slots outside the tile's budget are never written
+              if (lo_ + q >= 0 && lo_ + q < st) dst[lo_ + q] = (int32_t)((int64_t)t * CHUNK + x);
           const char* vrow = vbase + ((int64_t)t * CHUNK + x) * vstride;  // into the caches for the gather
           touch_to_lds4(vrow, lds_addr(pfsink));
           if constexpr (D * 2 > 128) touch_to_lds4(vrow + 128, lds_addr(pfsink));
@@ -939,6 +945,7 @@ decode_tail: __attribute__((unused));
           atomicOr(&bits[slot >> 5], 1u << (slot & 31));
         }
       }
+      zl = make_double2(tb.Z, 0.0);  // (read by the debug probabilities only)
     };
     if (!failed && headwave) {
       double* cg = cdfl + (size_t)hw * (T + 1);
@@ -952,7 +959,7 @@ decode_tail: __attribute__((unused));
         auto poll = [&](auto per) {
           constexpr int PER = decltype(per)::value;
           double mo[PER], lo[PER];
-          const int r = cdf_poll_to_lds<PER>(cmg, csg, T, lane, p.spin_limit, cg, sg, &zl, mo, lo);
+          const int r = cdf_poll_to_lds<PER, !DPROP>(cmg, csg, T, lane, p.spin_limit, cg, sg, &zl, mo, lo);
           if constexpr (DPROP) {
             if (r == 0) prop_counts(per, mo, lo);
           }
