@@ -651,6 +651,7 @@ constexpr int MODE_IID = 0, MODE_STRAT = 1, MODE_SYS = 2, MODE_PROP = 3, MODE_FL
 constexpr int KM_SCORE = 0;   // scores, statistics and prefix rows for the separate sampling kernel
 constexpr int KM_FLASH = 1;   // S²ANTA-flash kernel 1 fused in
 constexpr int KM_DECODE = 2;  // the whole decode step in one launch
-constexpr int KM_DECODE_PROP = 3;  // the same for S²ANTA-prop (tile budgets and per-key counts, no points)
+constexpr int KM_DECODE_PROP = 3;   // the same for S²ANTA-prop (tile budgets and per-key counts, no points)
+constexpr int KM_DECODE_FLASH = 4;  // the same for S²ANTA-flash (uniform tile budget, weighted gather)
 
 }  // namespace santa

@@ -21,6 +21,13 @@ hipError_t launch_decode_d(const Problem& p, hipStream_t st, const LaunchEvents&
     }
     return launch_timed(sk::score_stream_kernel<D, 2, KM_DECODE_PROP, 0>, grid, th, st, ev, p);
   }
+  if (p.mode == MODE_FLASH) {
+    if (p.G <= 4) {
+      if (n <= 4) return launch_timed(sk::score_stream_kernel<D, 1, KM_DECODE_FLASH, 4>, grid, th, st, ev, p);
+      return launch_timed(sk::score_stream_kernel<D, 1, KM_DECODE_FLASH, 0>, grid, th, st, ev, p);
+    }
+    return launch_timed(sk::score_stream_kernel<D, 2, KM_DECODE_FLASH, 0>, grid, th, st, ev, p);
+  }
   if (p.G <= 4) {
     if (n <= 4) return launch_timed(sk::score_stream_kernel<D, 1, KM_DECODE, 4>, grid, th, st, ev, p);
     return launch_timed(sk::score_stream_kernel<D, 1, KM_DECODE, 0>, grid, th, st, ev, p);

@@ -181,11 +181,11 @@ static_assert(MODE_IID == SANTA_IID && MODE_STRAT == SANTA_STRAT && MODE_SYS == 
               "the kernels number the sampling modes as the C header does");
 
 // The one-launch decode applies when the streaming score kernel runs (bf16, sequence-major K, G <= 8), the
-// sampling is i.i.d., stratified, systematic or S²ANTA-prop, every block of the grid fits on the device at
-// once (one per CU), the chunk CDF fits the in-kernel form and the sampling phase's LDS fits the K tiles.
+// sampling is any of the five modes, every block of the grid fits on the device at once (one per CU), the
+// chunk CDF fits the in-kernel form and the sampling phase's LDS fits the K tiles.
 // Returns the blocks per group, or 0 when the multi-launch path runs.
 int one_launch_blocks(const Problem& p, int cus) {
-  if (!p.bf16 || p.kfm || p.group_bern || p.mode > SANTA_PROP || p.G > MAX_GROUP || p.T > DECODE_MAX_T) return 0;
+  if (!p.bf16 || p.kfm || p.group_bern || p.mode > SANTA_FLASH || p.G > MAX_GROUP || p.T > DECODE_MAX_T) return 0;
   const int groups = p.B * p.Hkv;
   if (groups > cus || groups > SYNC_MAX_GROUPS) return 0;
   const int per = std::min(p.T, cus / groups);
@@ -301,6 +301,7 @@ int santa_decode_ex(const santa_args* a) {
   const int one = (a->mode & SANTA_MULTI_LAUNCH) ? 0 : one_launch_blocks(p, device_cus());
   p.one_launch = one > 0;
   if (p.one_launch) {
+    p.fused = false;  // S²ANTA-flash too runs in the one launch
     p.score_blocks_per_group = one;
     // the sampling phase's LDS plan for the largest chunk count of a block (checked to fit above)
     const DecodeLds L =

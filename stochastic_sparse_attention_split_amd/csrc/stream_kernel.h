@@ -5,7 +5,8 @@
 //   KM_DECODE: the whole decode step in one launch: after the score phase the blocks of a (KV head,
 //              sequence) group exchange their chunk statistics, then every block samples and gathers its
 //              own chunks and the group's output is summed (the tail of score_stream_kernel);
-//   KM_DECODE_PROP: the same for S²ANTA-prop (tile budgets and per-key counts instead of points).
+//   KM_DECODE_PROP, KM_DECODE_FLASH: the same for S²ANTA-prop and -flash (tile budgets and per-key
+//              counts instead of points).
 #pragma once
 
 #include "common.h"
@@ -279,8 +280,8 @@ __device__ inline bool wait_ge(int* ctr, int target, int limit) {
 template <int D, int HG, int KM, int NREG = 0>
 __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   constexpr bool FL = KM == KM_FLASH;
-  constexpr bool DEC = KM == KM_DECODE || KM == KM_DECODE_PROP;
-  constexpr bool DPROP = KM == KM_DECODE_PROP;
+  constexpr bool DEC = KM == KM_DECODE || KM == KM_DECODE_PROP || KM == KM_DECODE_FLASH;
+  constexpr bool DPROP = KM == KM_DECODE_PROP, DFLASH = KM == KM_DECODE_FLASH;
   static_assert(!FL || HG == 1, "the fused S²ANTA-flash form covers G <= 4");
   static_assert(NREG == 0 || (DEC && HG == 1), "register prefix rows: one-launch decode with G <= 4");
   constexpr int NRX = NREG > 0 ? NREG : 1;
@@ -319,6 +320,8 @@ __global__ __launch_bounds__(STHREADS, 1) void score_stream_kernel(Problem p) {
   // candidate counts of each chunk, per head
   __shared__ int rlo[DEC ? 8 : 1][DEC ? DECODE_MAX_CHUNKS : 1], rpre[DEC ? 8 : 1][DEC ? DECODE_MAX_CHUNKS + 1 : 1];
   __shared__ int wcnt[STHREADS / 64];
+  // one-launch S²ANTA-flash: weight W_t / (Z S_tile) of each head's count in each of the block's tiles
+  __shared__ float fw[KM == KM_DECODE_FLASH ? 8 : 1][KM == KM_DECODE_FLASH ? DECODE_MAX_CHUNKS : 1];
   double pv[NRX][4];            // one-launch decode, NREG > 0: this exponential wave's prefix rows
 
   // (chunk slot, KV head, sequence) of this block. The one-launch decode numbers the blocks XCD by XCD:
@@ -899,19 +902,46 @@ decode_tail: __attribute__((unused));
     const int64_t vstride = 2 * p.seq_stride;
     const char* vbase = (const char*)p.V + 2 * ((int64_t)b * p.batch_stride + (int64_t)kv * D);
     double2 zl = make_double2(0.0, 0.0);
+    // Per-tile systematic counts (KM_DECODE_PROP / _FLASH): tile t of head g with budget st > 0 gives key n of the
+    // block's chunk k the count c_n = floor(a0 + P_n st / l_t) - floor(a0 + P_{n-1} st / l_t) (lane l: keys
+    // 4 l .. 4 l + 3, P the in-chunk prefix), index slots [off + floor(..)) of the head's list, and its
+    // count and key bit for the gather.
+    auto count_tile = [&](int k, int t, int st, int off, double inv, double a0) {
+      const int g = hw, len = chunk_len(t);
+      const double* rw = NREG > 0 ? rows + ((size_t)g * LP.nb + k) * CHUNK
+                                  : p.stash + bhw * p.stash_stride + (int64_t)t * CHUNK;
+      int32_t* dst = p.idx + bhw * p.L + off;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int x = 4 * lane + i;
+        if (x >= len) continue;
+        const double ylo = a0 + inv * (x > 0 ? rw[x - 1] : 0.0);
+        const double yhi = a0 + inv * rw[x];
+        const int lo_ = (int)floor(ylo), hi_ = (int)floor(yhi);
+        const int c = hi_ > lo_ ? min(hi_ - lo_, st) : 0;
+        if (c == 0) continue;
+        if (p.want_idx)
+          for (int q = 0; q < c; ++q)  // slots outside the tile's budget are never written
+            if (lo_ + q >= 0 && lo_ + q < st) dst[lo_ + q] = (int32_t)((int64_t)t * CHUNK + x);
+        const char* vrow = vbase + ((int64_t)t * CHUNK + x) * vstride;  // into the caches for the gather
+        touch_to_lds4(vrow, lds_addr(pfsink));
+        if constexpr (D * 2 > 128) touch_to_lds4(vrow + 128, lds_addr(pfsink));
+        const int slot = k * CHUNK + x;
+        atomicAdd(&cnt[slot * NCW + (g >> 1)], (g & 1) ? ((uint32_t)c << 16) : (uint32_t)c);
+        atomicOr(&bits[slot >> 5], 1u << (slot & 31));
+      }
+    };
     // S²ANTA-prop ("Stochastic Sparse Attention for Memory-Bound Inference", Section 3.2; Appendix O,
     // Algorithms 4 and 5): the head's tile budgets S_t from every chunk's statistics (largest remainder,
-    // the multi-launch path's own code), then for each of the block's chunks with S_t > 0 the systematic
-    // counts c_n = floor(a0 + P_n S_t / l_t) - floor(a0 + P_{n-1} S_t / l_t) of its keys (lane l: keys
-    // 4 l .. 4 l + 3, P the in-chunk prefix), their slots [first slot of the tile + floor(..)) in the
-    // head's index list, and their counts and key bits for the gather. The outputs are (1/S) sum c_n v_n.
+    // the multi-launch path's own code), a0 from Philox counter (t, h, b, 3), the tile's first slot the
+    // budgets' exclusive prefix. The outputs are (1/S) sum c_n v_n.
     auto prop_counts = [&](auto per, const double* mo, const double* lo) {
       constexpr int PER = decltype(per)::value;
       TileBudgets<PER> tb;
       tile_budgets_wave<PER>(mo, lo, T, p.S, lane, reinterpret_cast<int*>(lds + p.lds_hist) + hw * 256, tb);
       const int g = hw, h = h0 + hw;
       for (int k = 0; k < n; ++k) {
-        const int t = t0 + k * P, len = chunk_len(t);
+        const int t = t0 + k * P;
         const int ol = t / PER, oj = t % PER;
         if (__builtin_expect(p.prob != nullptr, 0)) {  // for the debug probabilities below
           const double et = readlane_f64(pick<PER>(tb.e, oj), ol);  // (every lane forms its pick first)
@@ -921,31 +951,25 @@ decode_tail: __attribute__((unused));
         if (st == 0) continue;  // wave-uniform
         const int off = (int)readlane_f64(pick<PER>(tb.off, oj), ol);
         const double inv = (double)st / readlane_f64(pick<PER>(lo, oj), ol);
-        const double a0 = uniform53(p.seed, (uint32_t)t, (uint32_t)h, (uint32_t)b, TAG_PROP);
-        const double* rw = NREG > 0 ? rows + ((size_t)g * LP.nb + k) * CHUNK
-                                    : p.stash + bhw * p.stash_stride + (int64_t)t * CHUNK;
-        int32_t* dst = p.idx + bhw * p.L + off;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int x = 4 * lane + i;
-          if (x >= len) continue;
-          const double ylo = a0 + inv * (x > 0 ? rw[x - 1] : 0.0);
-          const double yhi = a0 + inv * rw[x];
-          const int lo_ = (int)floor(ylo), hi_ = (int)floor(yhi);
-          const int c = hi_ > lo_ ? min(hi_ - lo_, st) : 0;
-          if (c == 0) continue;
-          if (p.want_idx)
-            for (int q = 0; q < c; ++q)  // slots outside the tile's budget are never written
-              if (lo_ + q >= 0 && lo_ + q < st) dst[lo_ + q] = (int32_t)((int64_t)t * CHUNK + x);
-          const char* vrow = vbase + ((int64_t)t * CHUNK + x) * vstride;  // into the caches for the gather
-          touch_to_lds4(vrow, lds_addr(pfsink));
-          if constexpr (D * 2 > 128) touch_to_lds4(vrow + 128, lds_addr(pfsink));
-          const int slot = k * CHUNK + x;
-          atomicAdd(&cnt[slot * NCW + (g >> 1)], (g & 1) ? ((uint32_t)c << 16) : (uint32_t)c);
-          atomicOr(&bits[slot >> 5], 1u << (slot & 31));
-        }
+        count_tile(k, t, st, off, inv, uniform53(p.seed, (uint32_t)t, (uint32_t)h, (uint32_t)b, TAG_PROP));
       }
       zl = make_double2(tb.Z, 0.0);  // (read by the debug probabilities only)
+    };
+    // S²ANTA-flash (Section 3.3; Appendix P, Algorithms 6-8): every tile has the budget S_tile, slots
+    // [t S_tile, (t + 1) S_tile), a0 from Philox counter (t, h, b, 4); the gather weights the tile's counts
+    // by W_t / (Z S_tile), W_t = exp(m_t - m*) l_t from the chunk CDF's scales, and the outputs are the sums.
+    auto flash_counts = [&](auto per, const double* lo) {
+      constexpr int PER = decltype(per)::value;
+      const int g = hw, h = h0 + hw;
+      const int st = p.S_tile;
+      const double* sg = scl + (size_t)g * T;
+      for (int k = 0; k < n; ++k) {
+        const int t = t0 + k * P;
+        const double lt = readlane_f64(pick<PER>(lo, t % PER), t / PER);
+        if (lane == 0) fw[g][k] = (float)((sg[t] * lt) / (zl.x * (double)st));
+        count_tile(k, t, st, t * st, (double)st / lt,
+                   uniform53(p.seed, (uint32_t)t, (uint32_t)h, (uint32_t)b, TAG_FLASH));
+      }
     };
     if (!failed && headwave) {
       double* cg = cdfl + (size_t)hw * (T + 1);
@@ -959,9 +983,15 @@ decode_tail: __attribute__((unused));
         auto poll = [&](auto per) {
           constexpr int PER = decltype(per)::value;
           double mo[PER], lo[PER];
-          const int r = cdf_poll_to_lds<PER, !DPROP>(cmg, csg, T, lane, p.spin_limit, cg, sg, &zl, mo, lo);
-          if constexpr (DPROP) {
+          int r;
+          if constexpr (DFLASH) {
+            r = cdf_poll_to_lds<PER>(cmg, csg, T, lane, p.spin_limit, cg, sg, &zl, mo, lo);
+            if (r == 0) flash_counts(per, lo);
+          } else if constexpr (DPROP) {  // S²ANTA-prop: budgets, no chunk CDF
+            r = cdf_poll_to_lds<PER, false>(cmg, csg, T, lane, p.spin_limit, cg, sg, &zl, mo, lo);
             if (r == 0) prop_counts(per, mo, lo);
+          } else {
+            r = cdf_poll_to_lds<PER>(cmg, csg, T, lane, p.spin_limit, cg, sg, &zl, mo, lo);
           }
           return r;
         };
@@ -993,7 +1023,7 @@ decode_tail: __attribute__((unused));
       // sampling (its chunk found from the CDF); for stratified / systematic sampling point m lies in
       // [m/S, (m+1)/S), so chunk t can only hold m in [floor(S C_t / Z) - 1, floor(S C_{t+1} / Z) + 1]
       int lo = 0, np = 0;
-      if (lane < n && p.mode != 0 && !DPROP) {  // (S²ANTA-prop has no points)
+      if (lane < n && p.mode != 0 && !DPROP && !DFLASH) {  // (S²ANTA-prop and -flash have no points)
         const int t = t0 + lane * P;
         const double c0 = cg[t], c1 = cg[t + 1];
         if (c1 > c0 || t == lastc) {
@@ -1141,10 +1171,12 @@ decode_tail: __attribute__((unused));
       for (int u0 = rg; u0 < nu; u0 += 2 * NRG) {
         int64_t key[2];
         uint32_t cw[2][NCW];
+        int kc[2];
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {  // entries past the list re-read its last row, added with count 0
           const int u = u0 + k2 * NRG;
           const int s = list[min(u, nu - 1)];
+          kc[k2] = s / CHUNK;
           key[k2] = (int64_t)(t0 + (s / CHUNK) * P) * CHUNK + s % CHUNK;
 #pragma unroll
           for (int w = 0; w < NCW; ++w) cw[k2][w] = u < nu ? cnt[s * NCW + w] : 0u;
@@ -1159,7 +1191,8 @@ decode_tail: __attribute__((unused));
 #pragma unroll
           for (int g = 0; g < GM; ++g) {
             const uint32_t c32 = cw[k2][g >> 1];
-            const float c = (float)((g & 1) ? (c32 >> 16) : (c32 & 0xFFFFu));
+            float c = (float)((g & 1) ? (c32 >> 16) : (c32 & 0xFFFFu));
+            if constexpr (DFLASH) c *= fw[g < G ? g : 0][kc[k2]];  // S²ANTA-flash: times the tile weight
 #pragma unroll
             for (int e = 0; e < EPG; ++e) acc[g][e] += c * v[e];
           }
@@ -1234,7 +1267,8 @@ decode_tail: __attribute__((unused));
       if (q == 0) {
         const int o2 = o0 + e0, g = o2 / D, e = o2 % D;
         const int64_t dst = ((int64_t)b * p.H + h0 + g) * D + e;
-        ((uint16_t*)p.out)[dst] = poisoned ? (uint16_t)0x7FC0u : f64_to_bf16_rne(sum / (double)p.S);
+        const double o = DFLASH ? sum : sum / (double)p.S;  // (S²ANTA-flash: weighted already)
+        ((uint16_t*)p.out)[dst] = poisoned ? (uint16_t)0x7FC0u : f64_to_bf16_rne(o);
       }
     }
     if (ttid == 0) {

@@ -206,14 +206,16 @@ def test_flash_cases(case):
 
 
 def test_flash_launch_count():
-    """S²ANTA-flash samples inside the score pass for bf16 caches with G <= 4 (two launches: score pass and
-    merge); fp32 and G > 4 keep the separate sampling kernel (three launches)."""
+    """S²ANTA-flash with bf16 caches runs in the one-launch decode; with the multi-launch flag it samples
+    inside the score pass for G <= 4 (two launches: score pass and merge); fp32, and G > 4 on the
+    multi-launch path, keep the separate sampling kernel (three launches)."""
     dev = torch.device("cuda:0")
-    for (H, Hkv, dtype, want) in ((8, 2, "bf16", 2), (8, 2, "f32", 3), (12, 2, "bf16", 3)):
+    for (H, Hkv, dtype, want, want_multi) in ((8, 2, "bf16", 1, 2), (8, 2, "f32", 3, 3), (12, 2, "bf16", 1, 3)):
         q, K, V, _ = workloads.make_inputs(1, H, Hkv, 64, 1500, dtype=dtype, spikes_per_head=2, rng_seed=H)
         _, info = santa.decode(q.to(dev), K.to(dev), V.to(dev), 40, "flash", 1, stats=True)
-        log(f"flash H{H}/{Hkv} {dtype}: {info['launches']} launches")
-        assert info["launches"] == want
+        _, info_m = santa.decode(q.to(dev), K.to(dev), V.to(dev), 40, "flash", 1, stats=True, multi_launch=True)
+        log(f"flash H{H}/{Hkv} {dtype}: {info['launches']} launches, {info_m['launches']} multi-launch")
+        assert info["launches"] == want and info_m["launches"] == want_multi
 
 
 @pytest.mark.parametrize("S", [256, 2048])
@@ -552,6 +554,10 @@ ONE_LAUNCH_CASES = [
     (1, 28, 4, 128, 131072, "prop", 512, False, 40),   # S²ANTA-prop, G = 7, 512 tiles, 8 per block
     (2, 16, 2, 128, 20000, "prop", 96, False, 4),      # S²ANTA-prop, G = 8
     (3, 16, 8, 64, 25563, "prop", 64, True, 2),        # S²ANTA-prop, d = 64, ragged tail, ternary
+    (1, 32, 8, 128, 32768, "flash", 2048, False, 32),  # S²ANTA-flash at its 32k operating point
+    (1, 4, 1, 128, 30000, "flash", 300, False, 8),     # S²ANTA-flash, one chunk per block
+    (1, 28, 4, 128, 131072, "flash", 512, False, 40),  # S²ANTA-flash, G = 7, 512 tiles, 8 per block
+    (1, 14, 2, 64, 20000, "flash", 96, True, 4),       # S²ANTA-flash, G = 7, d = 64, ternary
 ]
 
 
@@ -569,11 +575,16 @@ def test_one_launch_matches_multi_launch(case):
     qd, Kd, Vd = q.to(dev), K.to(dev), V.to(dev)
     i1 = torch.empty((B, H, S), dtype=torch.int32, device=dev)
     i2 = torch.empty_like(i1)
+    if mode == "flash":  # T * S_tile index slots per head
+        T = (nk + 255) // 256
+        S_tile = max(1, (2 * S + T) // (2 * T))
+        i1 = torch.empty((B, H, T * S_tile), dtype=torch.int32, device=dev)
+        i2 = torch.empty_like(i1)
     o1, info1 = santa.decode(qd, Kd, Vd, S, mode, 3, ternary=tern, idx_out=i1, stats=True)
     o2, info2 = santa.decode(qd, Kd, Vd, S, mode, 3, ternary=tern, idx_out=i2, stats=True, multi_launch=True)
     torch.cuda.synchronize()
     log(f"  launches {info1['launches']} vs {info2['launches']}, unique rows {info1['unique_rows']}")
-    assert info1["launches"] == 1 and info2["launches"] >= 3
+    assert info1["launches"] == 1 and info2["launches"] >= (2 if mode == "flash" else 3)
     assert torch.equal(i1, i2)
     assert info1["group_unique_rows"] == info2["group_unique_rows"]
     assert float((o1.float() - o2.float()).abs().max()) <= 2e-2
