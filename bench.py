@@ -5,8 +5,9 @@ bf16 K/V cache of nk=32768 positions with 32 planted aligned keys per query head
 with S=256 (seeded synthetic inputs, resident in HBM before timing).
 
 A step is one call of santa_decode_ex, timed with HIP events on the launching stream. On this workload
-the call is one kernel launch (score phase, group barrier, chunk CDF, sampling, gather, output sum);
-other shapes run score -> sampling+gather per chunk -> merge. Before every timed step a 1 GiB in-place
+the call is one kernel launch (score phase, exchange of the chunk statistics, chunk CDF, sampling,
+gather, output sum), as it is for S2ANTA-prop and -flash on it; other shapes run score -> sampling+gather
+per chunk -> merge. Before every timed step a 1 GiB in-place
 update evicts K/V from the caches (the 256 MB Infinity Cache would otherwise hold the 64 MiB K), outside
 the events, like the cold-cache protocol of the paper's kernel benchmark (Appendix Q). Reported alongside:
   * the dense bf16 decode baseline of the same library on the same inputs and protocol;
