@@ -172,16 +172,17 @@ int santa_decode(const void* q, const void* K, const void* V, int64_t nk, int he
 /*
  * santa_decode_ex — the full form. Caller-owned workspace (`workspace`, `workspace_bytes`); never
  * allocates device memory. Calls sharing one workspace must not overlap.
- * One launch where it applies (bf16, sequence-major K, SANTA_IID / STRAT / SYS / PROP, at most one block
+ * One launch where it applies (bf16, sequence-major K, any of the five modes, at most one block
  * per CU for the whole grid, up to 512 chunks of 256 keys per sequence and 32 per block, and the block's
  * chunks fit the sampling phase's LDS): the split-K score pass, then, after an exchange of the chunk
  * statistics between the blocks of each (KV head, sequence) group (Section 3.1's global barrier, per
  * group; the blocks wait for the published values themselves), the chunk CDF, the points that fall in
  * each block's chunks (SANTA_PROP: every head's tile budgets, then the per-key counts of the block's
- * tiles), the gather of each distinct sampled row once per group into fp32 sums per head, and the sum of
- * the blocks' partials per head times 1/S. These barriers need every block of the launch resident
- * at once; if other work keeps blocks from running, the bounded waits give up and the call reports
- * SANTA_ERR_TIMEOUT (santa_status) with NaN outputs.
+ * tiles; SANTA_FLASH: the uniform per-tile budget, no CDF), the gather of each distinct sampled row once
+ * per group into fp32 sums per head (SANTA_FLASH: each count weighted by W_t / (Z S_tile)), and the sum of
+ * the blocks' partials per head times 1/S (SANTA_FLASH: the plain sum). These barriers need every block
+ * of the launch resident at once; if other work keeps blocks from running, the bounded waits give up
+ * and the call reports SANTA_ERR_TIMEOUT (santa_status) with NaN outputs.
  * Otherwise three or four kernels on `stream`: the split-K score pass; for more than 128 chunks of 256
  * keys, the chunk CDF per KV group (SANTA_PROP: the tile budgets per query head; SANTA_FLASH needs neither),
  * which the next kernel otherwise builds itself; the sampling and gather-add per (chunk, KV group) (each
