@@ -12,8 +12,8 @@ update evicts K/V from the caches (the 256 MB Infinity Cache would otherwise hol
 the events, like the cold-cache protocol of the paper's kernel benchmark (Appendix Q). Reported alongside:
   * the dense bf16 decode baseline of the same library on the same inputs and protocol;
   * the roofline of the dominant kernel (the one-launch decode kernel where it runs, else the score
-    kernel): its algorithmic bytes over its execution time, from HIP events recorded at the kernel's own
-    start and end (a separate pass, same protocol); its measured HBM bytes from the committed rocprofv3
+    kernel): its algorithmic bytes over its time from HIP events recorded with its launch (its dispatch
+    and execution; a separate pass, same protocol); its measured HBM bytes from the committed rocprofv3
     counter record while the kernel sources are unchanged; the device's read rate on the same K bytes from
     a streaming-read probe timed the same way;
   * the same step captured into a HIP graph and replayed (same protocol);
@@ -289,8 +289,8 @@ def main():
         del q8, K8, V8, ws8, dws8
 
     # the device's streaming read rate on the same K bytes under the same cold protocol, timed like the
-    # decode kernel (events at the kernel's own start and end): the practical ceiling of the K stream,
-    # beside the published peak
+    # decode kernel (events recorded with the launch: its dispatch and execution): the practical ceiling
+    # of the K stream, beside the published peak
     rscratch = torch.empty(int(santa.lib().santa_stream_read_scratch_bytes()), dtype=torch.uint8, device=dev)
     for _ in range(args.warmup):
         santa.stream_read(K, rscratch, stream)

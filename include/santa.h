@@ -136,12 +136,12 @@ typedef struct santa_args {
                                 for SANTA_FLASH): sampled key index of each point, in point order */
   double* prob_out;          /* device [batch, heads, nk]: softmax probabilities */
   santa_stats* stats_out;    /* host; the call synchronises the stream to fill it */
-  float* stage_ms;           /* host float[4], milliseconds; synchronises the stream. [0]: execution time of
-                                the score kernel (events HIP records at the kernel's own start and end; the
-                                whole decode for the one-launch form); [1]: from the end of the score
-                                kernel to an event after the chunk CDF and resolve launches; [2]: from there
-                                to an event after the merge launch; [3]: from the score kernel's start to
-                                that last event */
+  float* stage_ms;           /* host float[4], milliseconds; synchronises the stream. [0]: time of the
+                                score kernel (events HIP records with its launch, hipExtLaunchKernel: its
+                                dispatch and execution; the whole decode for the one-launch form); [1]:
+                                from the end of the score kernel to an event after the chunk CDF and
+                                resolve launches; [2]: from there to an event after the merge launch; [3]:
+                                from the score kernel's start event to that last event */
   /* SANTA_K_FEATURE_MAJOR only (elements); rows must hold at least nk rounded up to 8 and start 16-byte
      aligned */
   int64_t kt_row_stride;     /* between feature rows; 0 means nk rounded up to 8 */
@@ -247,8 +247,8 @@ double santa_exp_f64(double x);
  * CU), writing one XOR word per block into `scratch` (device memory of santa_stream_read_scratch_bytes()
  * bytes, contents meaningless): the read bandwidth the device reaches for that size and cache state.
  * bytes must be a positive multiple of 16 and src 16-byte aligned; asynchronous like the decode calls,
- * unless kernel_ms (host, optional) is given: then the call synchronises and stores the kernel's
- * execution time in milliseconds from events HIP records at the kernel's own start and end.
+ * unless kernel_ms (host, optional) is given: then the call synchronises and stores the kernel's time
+ * in milliseconds from events HIP records with its launch (its dispatch and execution).
  */
 int santa_stream_read(const void* src, size_t bytes, void* scratch, size_t scratch_bytes, void* stream,
                       float* kernel_ms);

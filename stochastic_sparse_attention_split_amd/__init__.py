@@ -349,7 +349,7 @@ def dense_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, *, nk: int |
 def stream_read(t: torch.Tensor, scratch: torch.Tensor | None = None, stream=None, kernel_time: bool = False):
     """Reads the bytes of a contiguous device tensor once through santa_stream_read (a bandwidth probe);
     returns the scratch tensor holding one XOR word per block, or (scratch, kernel milliseconds) with
-    kernel_time (events at the kernel's own start and end; synchronises)."""
+    kernel_time (events HIP records with the launch: its dispatch and execution; synchronises)."""
     if not t.is_contiguous():
         raise ValueError("stream_read needs a contiguous tensor")
     need = int(lib().santa_stream_read_scratch_bytes())

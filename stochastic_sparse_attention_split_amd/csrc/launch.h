@@ -8,8 +8,10 @@
 
 namespace santa {
 
-// Optional timing events of one launch. When set, HIP records them at the kernel's own start and end
-// (hipExtLaunchKernel), so their elapsed time is the kernel's execution without the gaps around it.
+// Optional timing events of one launch. When set, HIP records them with the launch itself
+// (hipExtLaunchKernel), so their elapsed time is the kernel's dispatch and execution without the gaps
+// between launches (a profiler's kernel duration, which starts when the first wave runs, is shorter by
+// the dispatch).
 struct LaunchEvents {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;

@@ -327,7 +327,7 @@ int santa_decode_ex(const santa_args* a) {
   }
   hipError_t e;
   (void)hipGetLastError();  // start from a clean error state
-  // with stage timing, HIP records e[0] and e[1] at the score kernel's own start and end
+  // with stage timing, HIP records e[0] and e[1] with the score kernel's launch (its dispatch and execution)
   LaunchEvents sev;
   if (ev.on) sev = LaunchEvents{ev.e[0], ev.e[1]};
   if (p.one_launch) {
