@@ -298,21 +298,34 @@ __device__ inline double point_of(uint64_t seed, int mode, int S, int m, int h, 
   return ((double)m + u_sys) / (double)S;
 }
 
+// Where entry e of a prefix row is stored: RowAt is the plain layout; RowSwz, the layout of the prefix rows
+// a block keeps in LDS, permutes each 16-entry block by (block index ^ k), k the row's chunk slot in the
+// block, so that the reads of a search over several rows (the same entry of different rows, or entry j
+// of different 16-entry blocks) fall in different LDS banks.
+struct RowAt {
+  __device__ int operator()(int e) const { return e; }
+};
+struct RowSwz {
+  int k;
+  __device__ int operator()(int e) const { return (e & ~15) | ((e ^ (e >> 4) ^ k) & 15); }
+};
+
 // search_chunk (below) in two rounds of independent loads (fewer dependent round trips, in LDS or in
 // device memory): the first 16-entry block whose last entry exceeds r (15 probes), then the first
-// entry of that block that does.
-__device__ inline int search_chunk16(const double* P, double f, double r) {
+// entry of that block that does. at(e) is where entry e is stored.
+template <class At = RowAt>
+__device__ inline int search_chunk16(const double* P, double f, double r, At at = At()) {
   static_assert(CHUNK == 256, "16 blocks of 16 entries");
   double v[15];
 #pragma unroll
-  for (int i = 0; i < 15; ++i) v[i] = P[16 * i + 15];
+  for (int i = 0; i < 15; ++i) v[i] = P[at(16 * i + 15)];
   int bi = 15;  // no earlier block qualifies: the answer, if any, is in the last one
 #pragma unroll
   for (int i = 14; i >= 0; --i)
     if (v[i] * f > r) bi = i;
   double w[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) w[j] = P[16 * bi + j];
+  for (int j = 0; j < 16; ++j) w[j] = P[at(16 * bi + j)];
   int j0 = 16;
 #pragma unroll
   for (int j = 15; j >= 0; --j)
@@ -332,10 +345,11 @@ __device__ inline int search_chunk(const double* P, double f, double r) {
   return lo < CHUNK ? lo : -1;
 }
 
-// last key of a chunk whose prefix grows (its last key with mass; 0 if none)
-__device__ inline int last_positive(const double* P, int len) {
+// last key of a chunk whose prefix grows (its last key with mass; 0 if none); at(e) as above
+template <class At = RowAt>
+__device__ inline int last_positive(const double* P, int len, At at = At()) {
   for (int j = len - 1; j > 0; --j)
-    if (P[j] > P[j - 1]) return j;
+    if (P[at(j)] > P[at(j - 1)]) return j;
   return 0;
 }
 

@@ -868,7 +868,8 @@ decode_tail: __attribute__((unused));
     uint32_t* bits = reinterpret_cast<uint32_t*>(lds + p.lds_bits);  // [n * CHUNK / 32] sampled-key bitmap
     double* cdfl = reinterpret_cast<double*>(lds + p.lds_cdf);       // [G][T + 1] chunk CDF C_t of each head
     double* scl = reinterpret_cast<double*>(lds + p.lds_scl);        // [G][T] chunk scales exp(m_t - m*)
-    double* rows = reinterpret_cast<double*>(lds + p.lds_rows);      // [G][nb][CHUNK] prefix rows (NREG > 0)
+    double* rows = reinterpret_cast<double*>(lds + p.lds_rows);      // [G][nb][CHUNK] prefix rows (NREG > 0),
+                                                                     // entry e of slot k at RowSwz{k}(e)
     const int nbits = (n * CHUNK + 31) / 32;
     for (int i = ttid; i < n * CHUNK * NCW; i += TT) cnt[i] = 0u;
     for (int i = ttid; i < nbits; i += TT) bits[i] = 0u;
@@ -886,7 +887,7 @@ decode_tail: __attribute__((unused));
         for (int kk = 0; kk < NREG; ++kk)
           if (kk < n)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rowg[kk * CHUNK + 4 * lane + i] = pv[kk][i];
+            for (int i = 0; i < 4; ++i) rowg[kk * CHUNK + RowSwz{kk}(4 * lane + i)] = pv[kk][i];
       }
     };
 
@@ -912,13 +913,14 @@ decode_tail: __attribute__((unused));
       const int g = hw, len = chunk_len(t);
       const double* rw = NREG > 0 ? rows + ((size_t)g * LP.nb + k) * CHUNK
                                   : p.stash + bhw * p.stash_stride + (int64_t)t * CHUNK;
+      auto at = [&](int e) { return NREG > 0 ? RowSwz{k}(e) : e; };  // (the LDS rows' layout)
       int32_t* dst = p.idx + bhw * p.L + off;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int x = 4 * lane + i;
         if (x >= len) continue;
-        const double ylo = a0 + inv * (x > 0 ? rw[x - 1] : 0.0);
-        const double yhi = a0 + inv * rw[x];
+        const double ylo = a0 + inv * (x > 0 ? rw[at(x - 1)] : 0.0);
+        const double yhi = a0 + inv * rw[at(x)];
         const int lo_ = (int)floor(ylo), hi_ = (int)floor(yhi);
         const int c = hi_ > lo_ ? min(hi_ - lo_, st) : 0;
         if (c == 0) continue;
@@ -1103,8 +1105,14 @@ decode_tail: __attribute__((unused));
         // the block's prefix rows: in LDS (NREG > 0), else in its own stores in device memory (its L2)
         const double* rw = NREG > 0 ? rows + ((size_t)g * LP.nb + k) * CHUNK
                                     : p.stash + bhw * p.stash_stride + (int64_t)t * CHUNK;
-        int j = y < Z ? search_chunk16(rw, sg[t], y - c0) : -1;
-        if (__builtin_expect(j < 0, 0)) j = last_positive(rw, len);  // at or beyond the total through rounding
+        int j;
+        if constexpr (NREG > 0) {  // (the LDS rows' layout)
+          j = y < Z ? search_chunk16(rw, sg[t], y - c0, RowSwz{k}) : -1;
+          if (__builtin_expect(j < 0, 0)) j = last_positive(rw, len, RowSwz{k});  // at or beyond the total
+        } else {
+          j = y < Z ? search_chunk16(rw, sg[t], y - c0) : -1;
+          if (__builtin_expect(j < 0, 0)) j = last_positive(rw, len);  // at or beyond the total through rounding
+        }
         j = min(j, len - 1);
         p.idx[bhw * p.S + m] = (int32_t)((int64_t)t * CHUNK + j);
         // the key's V row, brought into the caches now for the gather below: copies into a sink in LDS
