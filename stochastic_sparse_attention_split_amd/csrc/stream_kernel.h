@@ -99,10 +99,11 @@ __device__ inline int tile_off(int row, int pc) {
 // calls done(true) once every flag equals `target`, done(false) after `limit` checks. Up to 64 flags: four
 // rounds of loads, issued spaced in time and checked in order. (The compiler's wait at the head of the
 // loop covers every round in flight, so from the second sweep on the four rounds are checked together;
-// keeping them spaced, by unrolling the first sweeps, was measured slower: the extra device-scope loads
-// cost more than the earlier sight of the flags.) The rounds still in flight when the flags are seen are
-// retired after done() (a use of their registers, so the compiler's own wait lands there): code that
-// joins this wave's path afterwards finds no load of it outstanding.
+// keeping them spaced by unrolling the first sweeps, here and in the decode's other polls, was measured
+// no faster: the extra device-scope loads cost about what the earlier sight of the words gains.) The
+// rounds still in flight when the flags are seen are retired after done() (a use of their registers, so
+// the compiler's own wait lands there): code that joins this wave's path afterwards finds no load of it
+// outstanding.
 __device__ inline uint64_t ld_flag(const uint64_t* f) {
   return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
